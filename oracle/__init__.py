@@ -1,0 +1,272 @@
+"""CPU oracle for DFloat11-style lossless BF16 compression.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are its only users.  The product library never imports,
+links or calls anything here, and this package never imports the product.
+
+The arithmetic lives in ``df11_oracle.c`` (plain bit-serial C, built with gcc
+into ``libdf11_oracle.so``); this module only marshals numpy arrays into it and
+adds the closed-form quantities the checks need (entropy, Kraft sum, mean
+code length).  What each step follows on the pages is cited in the C file.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "df11_oracle.c")
+_LIB = os.path.join(_HERE, "libdf11_oracle.so")
+
+MAX_LEN = 32
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, nothing vectorised by hand)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared",
+                               _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        u64 = ctypes.c_uint64
+        u32 = ctypes.c_uint32
+        L.oracle_histogram.argtypes = [u16p, u64, u64p]
+        L.oracle_histogram.restype = None
+        L.oracle_huffman_lengths.argtypes = [u64p, u8p]
+        L.oracle_huffman_lengths.restype = ctypes.c_int
+        L.oracle_limited_lengths.argtypes = [u64p, ctypes.c_int, u8p]
+        L.oracle_limited_lengths.restype = ctypes.c_int
+        L.oracle_code_lengths.argtypes = [u64p, u8p]
+        L.oracle_code_lengths.restype = ctypes.c_int
+        L.oracle_canonical_codes.argtypes = [u8p, u32p]
+        L.oracle_canonical_codes.restype = None
+        L.oracle_encode.argtypes = [u16p, u64, u8p, u32p, u8p, u64, u8p, u64p]
+        L.oracle_encode.restype = ctypes.c_int
+        for name in ("oracle_aux", "oracle_aux_fast"):
+            f = getattr(L, name)
+            f.argtypes = [u16p, u64, u8p, u32, u32, u8p, u64, u32p, u64]
+            f.restype = ctypes.c_int
+        L.oracle_decode.argtypes = [u8p, u64, u64, u8p, u8p, u64, u16p]
+        L.oracle_decode.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, ct):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def _cat(tensors) -> np.ndarray:
+    if isinstance(tensors, np.ndarray):
+        tensors = [tensors]
+    parts = [np.ascontiguousarray(t, dtype=np.uint16).reshape(-1) for t in tensors]
+    if len(parts) == 1:
+        return parts[0]
+    return np.concatenate(parts)
+
+
+# ---------------------------------------------------------------- codebook
+
+
+def histogram(tensors) -> np.ndarray:
+    w = _cat(tensors)
+    c = np.zeros(256, dtype=np.uint64)
+    lib().oracle_histogram(_p(w, ctypes.c_uint16), w.size, _p(c, ctypes.c_uint64))
+    return c
+
+
+def huffman_lengths(counts) -> np.ndarray:
+    c = np.ascontiguousarray(counts, dtype=np.uint64)
+    assert c.size == 256
+    lens = np.zeros(256, dtype=np.uint8)
+    lib().oracle_huffman_lengths(_p(c, ctypes.c_uint64), _p(lens, ctypes.c_uint8))
+    return lens
+
+
+def limited_lengths(counts, limit: int) -> np.ndarray:
+    c = np.ascontiguousarray(counts, dtype=np.uint64)
+    assert c.size == 256
+    lens = np.zeros(256, dtype=np.uint8)
+    r = lib().oracle_limited_lengths(_p(c, ctypes.c_uint64), int(limit), _p(lens, ctypes.c_uint8))
+    if r < 0:
+        raise ValueError("more symbols than codes of the given limit")
+    return lens
+
+
+def code_lengths(counts) -> np.ndarray:
+    c = np.ascontiguousarray(counts, dtype=np.uint64)
+    lens = np.zeros(256, dtype=np.uint8)
+    lib().oracle_code_lengths(_p(c, ctypes.c_uint64), _p(lens, ctypes.c_uint8))
+    return lens
+
+
+def canonical_codes(lens) -> np.ndarray:
+    lens = np.ascontiguousarray(lens, dtype=np.uint8)
+    codes = np.zeros(256, dtype=np.uint32)
+    lib().oracle_canonical_codes(_p(lens, ctypes.c_uint8), _p(codes, ctypes.c_uint32))
+    return codes
+
+
+@dataclass
+class Codebook:
+    counts: np.ndarray
+    lens: np.ndarray
+    codes: np.ndarray
+
+
+def codebook(tensors) -> Codebook:
+    counts = histogram(tensors)
+    lens = code_lengths(counts)
+    return Codebook(counts, lens, canonical_codes(lens))
+
+
+# ---------------------------------------------------------------- stream
+
+
+@dataclass
+class Encoded:
+    stream: np.ndarray        # uint8, ceil(total_bits / 8) bytes
+    sm: np.ndarray            # uint8, one per weight
+    total_bits: int
+    tensor_start_bits: list   # start bit of each input tensor, plus total_bits
+    numel: list
+
+
+def encode(tensors, cb: Codebook) -> Encoded:
+    if isinstance(tensors, np.ndarray):
+        tensors = [tensors]
+    w = _cat(tensors)
+    lens = np.ascontiguousarray(cb.lens, dtype=np.uint8)
+    codes = np.ascontiguousarray(cb.codes, dtype=np.uint32)
+    total = int(sum(int(lens[(int(e))]) * int(c) for e, c in enumerate(histogram(w))))
+    stream = np.zeros(max(1, (total + 7) // 8), dtype=np.uint8)
+    sm = np.zeros(w.size, dtype=np.uint8)
+    tb = np.zeros(1, dtype=np.uint64)
+    r = lib().oracle_encode(_p(w, ctypes.c_uint16), w.size, _p(lens, ctypes.c_uint8),
+                            _p(codes, ctypes.c_uint32), _p(stream, ctypes.c_uint8), stream.size,
+                            _p(sm, ctypes.c_uint8), _p(tb, ctypes.c_uint64))
+    if r != 0:
+        raise ValueError(f"oracle_encode failed ({r})")
+    assert int(tb[0]) == total
+    starts = [0]
+    numel = []
+    for t in tensors:
+        t = np.ascontiguousarray(t, dtype=np.uint16).reshape(-1)
+        h = histogram(t)
+        starts.append(starts[-1] + int(sum(int(lens[e]) * int(c) for e, c in enumerate(h))))
+        numel.append(t.size)
+    return Encoded(stream[: (total + 7) // 8], sm, total, starts, numel)
+
+
+def aux(tensors, cb: Codebook, threads: int, bytes_per_thread: int, fast: bool = True):
+    """(gaps uint8[n_tiles*threads], block_out_pos uint32[n_tiles+1]) from the definitions."""
+    w = _cat(tensors)
+    lens = np.ascontiguousarray(cb.lens, dtype=np.uint8)
+    total = int(sum(int(lens[e]) * int(c) for e, c in enumerate(histogram(w))))
+    window_bits = 8 * bytes_per_thread
+    tile_bits = window_bits * threads
+    n_tiles = (total + tile_bits - 1) // tile_bits
+    gaps = np.zeros(n_tiles * threads, dtype=np.uint8)
+    bop = np.zeros(n_tiles + 1, dtype=np.uint32)
+    f = lib().oracle_aux_fast if fast else lib().oracle_aux
+    r = f(_p(w, ctypes.c_uint16), w.size, _p(lens, ctypes.c_uint8), window_bits, threads,
+          _p(gaps, ctypes.c_uint8), gaps.size, _p(bop, ctypes.c_uint32), n_tiles)
+    if r != 0:
+        raise ValueError(f"oracle_aux failed ({r})")
+    return gaps, bop
+
+
+def decode(stream: np.ndarray, start_bit: int, end_bit: int, lens, sm: np.ndarray,
+           n: int | None = None) -> np.ndarray:
+    """Bit-serial decode of n symbols from start_bit; returns uint16 BF16 bit patterns."""
+    stream = np.ascontiguousarray(stream, dtype=np.uint8)
+    lens = np.ascontiguousarray(lens, dtype=np.uint8)
+    sm = np.ascontiguousarray(sm, dtype=np.uint8)
+    if n is None:
+        n = sm.size
+    assert sm.size >= n
+    out = np.zeros(n, dtype=np.uint16)
+    if n == 0:
+        return out
+    r = lib().oracle_decode(_p(stream, ctypes.c_uint8), start_bit, end_bit,
+                            _p(lens, ctypes.c_uint8), _p(sm, ctypes.c_uint8), n,
+                            _p(out, ctypes.c_uint16))
+    if r != 0:
+        raise ValueError(f"oracle_decode failed ({r})")
+    return out
+
+
+# ---------------------------------------------------------------- closed forms
+
+
+def entropy_bits(counts) -> float:
+    """Shannon entropy H = -sum p log2 p of the exponent histogram, in float64."""
+    c = np.asarray(counts, dtype=np.float64)
+    n = c.sum()
+    if n == 0:
+        return 0.0
+    p = c[c > 0] / n
+    return float(-(p * np.log2(p)).sum())
+
+
+def mean_code_length(counts, lens) -> float:
+    c = np.asarray(counts, dtype=np.float64)
+    n = c.sum()
+    return float((c * np.asarray(lens, dtype=np.float64)).sum() / n) if n else 0.0
+
+
+def total_code_bits(counts, lens) -> int:
+    return int(sum(int(c) * int(l) for c, l in zip(np.asarray(counts), np.asarray(lens))))
+
+
+def kraft_numerator(lens) -> int:
+    """sum over coded symbols of 2^(32 - l): equals 2^32 exactly for a complete code."""
+    return int(sum(1 << (MAX_LEN - int(l)) for l in np.asarray(lens) if int(l) > 0))
+
+
+def sign_mantissa(w: np.ndarray) -> np.ndarray:
+    w = np.asarray(w, dtype=np.uint16)
+    return (((w >> 8) & 0x80) | (w & 0x7F)).astype(np.uint8)
+
+
+def exponents(w: np.ndarray) -> np.ndarray:
+    return ((np.asarray(w, dtype=np.uint16) >> 7) & 0xFF).astype(np.uint8)
+
+
+def gaussian_exponent_probs(sigma: float) -> np.ndarray:
+    """Closed-form probability that a N(0, sigma^2) value lands in BF16 binade e.
+
+    For normal binades, |x| in [2^(e-127), 2^(e-126)) has probability
+    2 * (Phi(2^(e-126)/sigma) - Phi(2^(e-127)/sigma)); e = 0 (zero and
+    subnormals) takes |x| < 2^-126.  Rounding at binade edges is ignored.
+    """
+    phi = lambda x: 0.5 * (1.0 + math.erf(x / math.sqrt(2.0)))
+    p = np.zeros(256)
+    p[0] = 2.0 * (phi(2.0 ** -126 / sigma) - 0.5)
+    for e in range(1, 255):
+        lo, hi = 2.0 ** (e - 127), 2.0 ** (e - 126)
+        p[e] = 2.0 * (phi(hi / sigma) - phi(lo / sigma))
+    return p

@@ -1,0 +1,334 @@
+"""Pins for the CPU oracle, checked against what the pages and mathematics fix.
+
+Nothing here re-types the oracle's own formulas: each check comes from a
+published worked example, a brute-force search, a closed form, an invariant
+of optimal prefix codes, or an independent consumer of the oracle's output.
+"""
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _counts(d):
+    c = np.zeros(256, dtype=np.uint64)
+    for s, v in d.items():
+        c[s] = v
+    return c
+
+
+def _cost(counts, lens):
+    return sum(int(c) * int(l) for c, l in zip(counts, lens))
+
+
+def _brute_min_cost(weights, max_len):
+    """Minimum sum(w*l) over all length vectors in [1, max_len]^n with Kraft <= 1."""
+    n = len(weights)
+    best = None
+    for ls in itertools.product(range(1, max_len + 1), repeat=n):
+        if sum(2.0 ** -l for l in ls) <= 1.0 + 1e-12:
+            c = sum(w * l for w, l in zip(weights, ls))
+            if best is None or c < best:
+                best = c
+    return best
+
+
+# ------------------------------------------------------------ worked examples
+
+
+def test_golden_textbook_huffman_lengths():
+    rows = _read_golden("clrs_huffman.txt")
+    counts = _counts({int(s): int(f) for s, f, _ in rows})
+    lens = oracle.huffman_lengths(counts)
+    for s, _, l in rows:
+        assert lens[int(s)] == int(l)
+    assert _cost(counts, lens) == 224
+    assert (lens[6:] == 0).all()
+
+
+def test_golden_rfc1951_canonical_codes():
+    rows = _read_golden("rfc1951_canonical.txt")
+    lens = np.zeros(256, dtype=np.uint8)
+    for s, l, _ in rows:
+        lens[int(s)] = int(l)
+    codes = oracle.canonical_codes(lens)
+    for s, l, bits in rows:
+        assert format(int(codes[int(s)]), f"0{int(l)}b") == bits
+    # the decoder derives its own tables from the lengths: decode the golden codes
+    bitstr = "".join(b for _, _, b in rows)
+    nbits = len(bitstr)
+    stream = np.zeros((nbits + 7) // 8, dtype=np.uint8)
+    for i, ch in enumerate(bitstr):
+        if ch == "1":
+            stream[i // 8] |= 0x80 >> (i % 8)
+    sm = np.zeros(len(rows), dtype=np.uint8)
+    out = oracle.decode(stream, 0, nbits, lens, sm)
+    assert [int(v) >> 7 for v in out] == [int(s) for s, _, _ in rows]
+
+
+# ------------------------------------------------------------ optimality
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_huffman_cost_equals_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 7))
+    weights = [int(x) for x in rng.integers(1, 50, size=n)]
+    syms = rng.choice(256, size=n, replace=False)
+    counts = _counts(dict(zip(syms.tolist(), weights)))
+    lens = oracle.huffman_lengths(counts)
+    assert _cost(counts, lens) == _brute_min_cost(weights, n - 1)
+
+
+def test_huffman_ties_have_equal_cost():
+    # {1, 1, 2, 2} admits both {2,2,2,2} and {3,3,2,1}: only the cost is unique
+    counts = _counts({10: 1, 11: 1, 12: 2, 13: 2})
+    lens = oracle.huffman_lengths(counts)
+    assert _cost(counts, lens) == 12 == _brute_min_cost([1, 1, 2, 2], 3)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_package_merge_equals_bounded_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    n, limit = 6, 3
+    weights = [int(x) for x in rng.integers(1, 1000, size=n) ** 2]
+    counts = _counts(dict(enumerate(weights)))
+    lens = oracle.limited_lengths(counts, limit)
+    assert lens[:n].max() <= limit
+    assert oracle.kraft_numerator(lens) <= 1 << 32
+    assert _cost(counts, lens) == _brute_min_cost(weights, limit)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_package_merge_matches_huffman_when_limit_is_loose(seed):
+    rng = np.random.default_rng(200 + seed)
+    counts = rng.integers(0, 10_000, size=256).astype(np.uint64)
+    counts[rng.random(256) < 0.5] = 0
+    h = oracle.huffman_lengths(counts)
+    pm = oracle.limited_lengths(counts, int(h.max()))
+    assert _cost(counts, pm) == _cost(counts, h)
+
+
+def _fibonacci_counts(n):
+    f = [1, 1]
+    while len(f) < n:
+        f.append(f[-1] + f[-2])
+    return _counts(dict(enumerate(f)))
+
+
+def test_length_limit_forced_by_fibonacci_histogram():
+    counts = _fibonacci_counts(40)
+    h = oracle.huffman_lengths(counts)
+    assert h.max() == 39  # natural depth n - 1
+    lens = oracle.code_lengths(counts)
+    assert lens.max() == 32
+    assert oracle.kraft_numerator(lens) == 1 << 32
+    assert _cost(counts, lens) >= _cost(counts, h)
+    # still optimal among codes with l <= 32: package-merge at 32 vs at 33..39 is monotone
+    assert _cost(counts, oracle.limited_lengths(counts, 33)) <= _cost(counts, lens)
+
+
+# ------------------------------------------------------------ invariants
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_kraft_sum_is_exactly_one(seed):
+    rng = np.random.default_rng(300 + seed)
+    counts = (rng.pareto(1.0, size=256) * 1000).astype(np.uint64)
+    counts[rng.random(256) < rng.random()] = 0
+    if (counts > 0).sum() < 1:
+        counts[7] = 3
+    lens = oracle.code_lengths(counts)
+    assert oracle.kraft_numerator(lens) == 1 << 32
+
+
+def test_dyadic_counts_give_exact_lengths_and_entropy():
+    # p = 2^-k: Huffman reaches the entropy exactly with l_s = k
+    d = {40: 1 << 10, 41: 1 << 9, 42: 1 << 8, 43: 1 << 7, 44: 1 << 6, 45: 1 << 6}
+    counts = _counts(d)
+    lens = oracle.huffman_lengths(counts)
+    n = sum(d.values())
+    for s, c in d.items():
+        assert lens[s] == int(round(-math.log2(c / n)))
+    assert oracle.mean_code_length(counts, lens) == pytest.approx(oracle.entropy_bits(counts), abs=1e-12)
+
+
+def test_two_symbols_have_length_one():
+    lens = oracle.huffman_lengths(_counts({3: 1000, 200: 1}))
+    assert lens[3] == 1 and lens[200] == 1 and lens.sum() == 2
+
+
+def test_single_symbol_gets_a_dummy_partner():
+    w = np.full(1000, (127 << 7) | 5, dtype=np.uint16)  # exponent 127 only
+    cb = oracle.codebook(w)
+    assert cb.lens[127] == 1 and cb.lens[0] == 1 and (cb.lens > 0).sum() == 2
+    assert oracle.kraft_numerator(cb.lens) == 1 << 32
+    enc = oracle.encode(w, cb)
+    assert enc.total_bits == 1000
+    # the dummy (value 0) sorts first and takes code 0, so every code is a 1 bit
+    assert (enc.stream[:125] == 0xFF).all()
+    assert np.array_equal(oracle.decode(enc.stream, 0, enc.total_bits, cb.lens, enc.sm), w)
+
+
+def test_uniform_256_exponents_stream_is_the_exponent_bytes():
+    rng = np.random.default_rng(5)
+    e = np.repeat(np.arange(256, dtype=np.uint16), 64)
+    rng.shuffle(e)
+    w = (e << 7) | rng.integers(0, 1 << 16, size=e.size, dtype=np.uint16) & np.uint16(0x807F)
+    cb = oracle.codebook(w)
+    assert (cb.lens == 8).all()
+    assert np.array_equal(cb.codes, np.arange(256, dtype=np.uint32))
+    enc = oracle.encode(w, cb)
+    assert np.array_equal(enc.stream, e.astype(np.uint8))
+    gaps, bop = oracle.aux(w, cb, threads=4, bytes_per_thread=8)
+    assert (gaps == 0).all()
+    assert np.array_equal(bop, np.minimum(np.arange(bop.size) * 32, e.size).astype(np.uint32))
+
+
+# ------------------------------------------------------------ round trips
+
+
+def _round_trip(w):
+    cb = oracle.codebook(w)
+    enc = oracle.encode(w, cb)
+    out = oracle.decode(enc.stream, 0, enc.total_bits, cb.lens, enc.sm)
+    assert np.array_equal(out, w)
+    return cb, enc
+
+
+def test_round_trip_every_bit_pattern():
+    w = np.arange(1 << 16, dtype=np.uint16)
+    np.random.default_rng(6).shuffle(w)
+    cb, _ = _round_trip(w)
+    assert (cb.lens == 8).all()
+
+
+def test_round_trip_special_values():
+    specials = [0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81, 0x0001, 0x807F,
+                0x0080, 0x3F80, 0xBF80, 0x7F7F, 0xFF7F]
+    w = np.array(specials * 37, dtype=np.uint16)
+    _round_trip(w)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 64, 1000, 4097])
+def test_round_trip_small_sizes(n):
+    rng = np.random.default_rng(n)
+    w = (rng.standard_normal(n).astype(np.float32) * 0.02).view(np.uint32) >> 16
+    _round_trip(w.astype(np.uint16))
+
+
+def test_sign_mantissa_byte_layout_from_the_bf16_fields():
+    # sign is bit 15, exponent bits 14..7, mantissa bits 6..0 of a BF16 pattern
+    w = np.array([0b1_10000001_0101010, 0b0_01111111_1111111], dtype=np.uint16)
+    cb, enc = _round_trip(w)
+    assert enc.sm.tolist() == [0b1_0101010, 0b0_1111111]
+    assert oracle.exponents(w).tolist() == [0b10000001, 0b01111111]
+
+
+# ------------------------------------------------------------ aux arrays
+
+
+def _py_decode_windows(stream, total_bits, lens, codes, gaps, bop, threads, bpt):
+    """Independent consumer of the aux arrays: decode each window from its gap
+    with a dict lookup, stopping at the first code that starts past the window."""
+    table = {(int(l), int(codes[s])): s for s, l in enumerate(lens) if l}
+    bits = np.unpackbits(np.asarray(stream, dtype=np.uint8))
+    wb = 8 * bpt
+    syms = []
+    per_tile = []
+    for j, g in enumerate(gaps):
+        if j % threads == 0:
+            per_tile.append(len(syms))
+        if g == 255:
+            continue
+        assert g < 32
+        p = j * wb + int(g)
+        while p < min((j + 1) * wb, total_bits):
+            v, l = 0, 0
+            while (l, v) not in table or l == 0:
+                v = (v << 1) | int(bits[p + l])
+                l += 1
+                assert l <= 32
+            syms.append(table[(l, v)])
+            p += l
+    per_tile.append(len(syms))
+    assert per_tile == [int(x) for x in bop]
+    return syms
+
+
+@pytest.mark.parametrize("threads,bpt", [(4, 8), (8, 16), (3, 8)])
+def test_aux_arrays_drive_an_independent_window_decoder(threads, bpt):
+    rng = np.random.default_rng(threads * 100 + bpt)
+    w = (rng.standard_normal(5000).astype(np.float32) * 0.02).view(np.uint32) >> 16
+    w = w.astype(np.uint16)
+    w[::97] = 0x7F80  # a few rare, long codes
+    cb = oracle.codebook(w)
+    enc = oracle.encode(w, cb)
+    gaps, bop = oracle.aux(w, cb, threads, bpt)
+    g2, b2 = oracle.aux(w, cb, threads, bpt, fast=False)
+    assert np.array_equal(gaps, g2) and np.array_equal(bop, b2)
+    padded = np.zeros(gaps.size * bpt + 8, dtype=np.uint8)
+    padded[: enc.stream.size] = enc.stream
+    syms = _py_decode_windows(padded, enc.total_bits, cb.lens, cb.codes, gaps, bop, threads, bpt)
+    assert syms == oracle.exponents(w).tolist()
+    assert bop[-1] == w.size
+
+
+# ------------------------------------------------------------ the pages' numbers
+
+
+def test_gaussian_histogram_matches_closed_form(unit_tensors):
+    (w,) = unit_tensors("0")
+    counts = oracle.histogram(w).astype(np.float64)
+    p = oracle.gaussian_exponent_probs(0.02)
+    n = counts.sum()
+    # binomial standard error per bin, plus rounding drift at binade edges (~2^-8 relative)
+    for e in range(110, 127):
+        expected = p[e] * n
+        tol = 6 * math.sqrt(expected + 1) + expected * 2.0 ** -7
+        assert abs(counts[e] - expected) < tol, e
+    assert int(np.argmax(counts)) == 121
+    assert oracle.entropy_bits(counts) == pytest.approx(oracle.entropy_bits(p * n), abs=0.01)
+
+
+@pytest.mark.parametrize("cfg,lo,hi", [("0", 10.0, 12.0), ("3a", 10.0, 12.0),
+                                       ("3b", 8.0, 10.0), ("3c", 16.0, 16.0)])
+def test_entropy_bound_and_bits_per_weight(unit_tensors, cfg, lo, hi):
+    (w,) = unit_tensors(cfg)
+    cb = oracle.codebook(w)
+    H = oracle.entropy_bits(cb.counts)
+    L = oracle.mean_code_length(cb.counts, cb.lens)
+    assert H - 1e-9 <= L < H + 1
+    assert oracle.kraft_numerator(cb.lens) == 1 << 32
+    # about 11 bits/weight (roughly 30% smaller than BF16) on Gaussian-like weights
+    assert lo <= 8 + L <= hi
+
+
+def test_heavy_tail_config_reaches_the_fourth_lut_level(unit_tensors):
+    (w,) = unit_tensors("3a")
+    cb = oracle.codebook(w)
+    assert cb.lens.max() > 24
+
+
+def test_round_trip_stress_configs(unit_tensors):
+    for cfg in ("3a", "3b", "3c"):
+        (w,) = unit_tensors(cfg)
+        w = w[: 1 << 21]
+        _round_trip(w)
