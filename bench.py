@@ -1,0 +1,319 @@
+"""Decompression throughput of the DFloat11-style BF16 decoder on one MI355X.
+
+One step = one df11_decompress_block launch over a whole unit (by default the
+Llama-3-70B-shaped transformer block: 855,638,016 BF16 weights, one codebook,
+one launch), with the compressed unit already resident in HBM.
+
+Prints one JSON line: value = decompressed BF16 GB/s (2 bytes per weight
+written, whole job over K steps), plus the dominant kernel's HBM roofline
+fraction from algorithmic bytes (compressed arrays read once + BF16 written)
+and the CPU oracle's bit-serial decode timed on this host as a baseline.
+
+  python bench.py [--steps K] [--warmup W] [--config 2|1|0|3a|3b|3c|4] [--bpt 8|16]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import subprocess
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "entropy_decoding_amd", "csrc", "df11_device.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(hs, cb) -> int:
+    """Compressed arrays read once (stream payload, sm, gaps, block_out_pos, tables)
+    plus 2 bytes of BF16 written per weight."""
+    read = (hs.total_bits + 7) // 8 + hs.n_weights + hs.gaps.size + 4 * hs.block_out_pos.size \
+        + 512 * cb.n_luts
+    return int(read + 2 * hs.n_weights)
+
+
+def measured_traffic(workload: str, bpt: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    r = rec.get(f"{workload}/B{bpt}")
+    if not r or r.get("kernel_sha") != kernel_hash():
+        return None
+    return r.get("bytes_per_launch")
+
+
+def cpu_name() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(tensors, seconds_budget: float = 30.0):
+    """The oracle's bit-serial decode on this host: one thread per tensor (each
+    tensor encoded by the oracle with the unit's codebook first, untimed)."""
+    import oracle
+
+    ocb = oracle.codebook(tensors)
+    encs = [None] * len(tensors)
+
+    def enc(i):
+        encs[i] = oracle.encode([tensors[i]], ocb)
+
+    ths = [threading.Thread(target=enc, args=(i,)) for i in range(len(tensors))]
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    outs = [None] * len(tensors)
+
+    def dec(i):
+        e = encs[i]
+        outs[i] = oracle.decode(e.stream, 0, e.total_bits, ocb.lens, e.sm)
+
+    ths = [threading.Thread(target=dec, args=(i,)) for i in range(len(tensors))]
+    t0 = time.perf_counter()
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    dt = time.perf_counter() - t0
+    for o, t in zip(outs, tensors):
+        assert np.array_equal(o, t), "oracle decode is not lossless"
+    n = sum(t.size for t in tensors)
+    return {"value": round(2 * n / dt / 1e9, 4), "unit": "GB/s", "cores": len(tensors),
+            "kind": "oracle",
+            "sample": f"all {len(tensors)} tensors of the unit ({n} weights), one thread per "
+                      f"tensor, bit-serial canonical decode, {dt:.2f} s wall on {cpu_name()} "
+                      f"(nproc={os.cpu_count()})"}
+
+
+def run_unit(name, tensors, args, torch, ed):
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    cb = ed.df11_build_codebook(tensors)
+    hs = ed.df11_encode(cb, tensors, 256, args.bpt)
+    log(f"[bench] {name}: encoded {hs.n_weights} weights in {time.perf_counter() - t0:.1f} s, "
+        f"{hs.n_tiles} tiles, luts={cb.n_luts}, max_len={cb.max_len}")
+    ds = ed.DeviceStream(hs, cb, dev)
+    n = hs.n_weights
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    alg = algorithmic_bytes(hs, cb)
+    small = alg < (1 << 30)  # fits the 256 MB last-level cache several times over: flush
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev) if small else None
+
+    for _ in range(args.warmup):
+        ed.df11_decompress_block(ds, out, status, stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        starts[i].record(stream)
+        ed.df11_decompress_block(ds, out, status, stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    st = int(status.item())
+    ref = torch.from_numpy(np.concatenate([np.asarray(t).reshape(-1) for t in tensors])
+                           .view(np.int16)).to(dev)
+    exact = st == 0 and torch.equal(out.view(torch.int16), ref)
+    del ref
+    payload = 8 + hs.total_bits / n
+    total_bits = 8 * (sum(hs.compressed_bytes(cb).values())) / n
+    return {
+        "name": name, "n": n, "hs": hs, "cb": cb, "kernel_ms": kms, "wall_s": wall,
+        "alg_bytes": alg, "exact": exact, "status": st, "payload_bpw": payload,
+        "total_bpw": total_bits, "flushed": small,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2")
+    ap.add_argument("--bpt", type=int, default=8, choices=(8, 16))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the decoder needs no cross-GPU exchange and this "
+              f"build runs on a single MI355X; --gpus {args.gpus} is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import entropy_decoding_amd as ed
+    import synth_weights as sw
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    cfg = sw.config(args.config)
+    if len(cfg.units) != 1:
+        return stream_units(cfg, args, torch, ed, sw)
+    unit = cfg.units[0]
+    t0 = time.perf_counter()
+    tensors = sw.gen_unit(unit)
+    log(f"[bench] generated {cfg.name} ({unit.numel} weights) in {time.perf_counter() - t0:.1f} s")
+    r = run_unit(cfg.name, tensors, args, torch, ed)
+    kms = r["kernel_ms"]
+    avg_ms = float(kms.mean())
+    n = r["n"]
+    achieved = r["alg_bytes"] / (avg_ms * 1e-3) / 1e9
+    if r["flushed"]:
+        value = 2 * n * args.steps / (kms.sum() * 1e-3) / 1e9  # flush kernels excluded
+    else:
+        value = 2 * n * args.steps / r["wall_s"] / 1e9
+    traffic = measured_traffic(cfg.name, args.bpt)
+    line = {
+        "metric": "decompressed BF16 GB/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_s"] * 1e3 / args.steps if not r["flushed"] else avg_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "n_weights": n,
+            "layout": f"T256xB{args.bpt}",
+            "bit_exact": bool(r["exact"]),
+            "bits_per_weight_payload": round(r["payload_bpw"], 4),
+            "bits_per_weight_total": round(r["total_bpw"], 4),
+            "size_vs_bf16": round(r["total_bpw"] / 16, 4),
+            "kernel_ms_p50": round(float(np.percentile(kms, 50)), 4),
+            "kernel_ms_p99": round(float(np.percentile(kms, 99)), 4),
+            "caches_flushed_between_steps": r["flushed"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(tensors)
+    print(json.dumps(line), flush=True)
+    if not r["exact"]:
+        sys.exit(1)
+
+
+def stream_units(cfg, args, torch, ed, sw):
+    """Several units: each compressed unit resident in HBM, decompressed in
+    order into one reused output buffer; per-unit latency from HIP events."""
+    dev = torch.device("cuda:0")
+    units = []
+    t0 = time.perf_counter()
+    for unit in cfg.units:
+        tensors = sw.gen_unit(unit)
+        cb = ed.df11_build_codebook(tensors)
+        hs = ed.df11_encode(cb, tensors, 256, args.bpt)
+        ds = ed.DeviceStream(hs, cb, dev)
+        ref_hash = None
+        units.append((unit, ds, hs, cb, tensors if cfg.index != 4 else None))
+        log(f"[bench] {unit.name}: {hs.n_weights} weights resident "
+            f"({time.perf_counter() - t0:.0f} s)")
+        del tensors, ref_hash
+    nmax = max(u[2].n_weights for u in units)
+    out = torch.empty(nmax, dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for u in units:
+            ed.df11_decompress_block(u[1], out, status, stream)
+    torch.cuda.synchronize()
+    passes = max(1, args.steps)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in units] for _ in range(passes)]
+    t0 = time.perf_counter()
+    for p in range(passes):
+        for i, u in enumerate(units):
+            ev[p][i][0].record(stream)
+            ed.df11_decompress_block(u[1], out, status, stream)
+            ev[p][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lat = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
+    n_total = sum(u[2].n_weights for u in units)
+    alg = sum(algorithmic_bytes(u[2], u[3]) for u in units)
+    # bit-exactness: every unit once more, compared with regenerated originals
+    exact = int(status.item()) == 0
+    for unit, ds, hs, cb, tensors in units:
+        if tensors is None:
+            tensors = sw.gen_unit(unit)
+        ed.df11_decompress_block(ds, out, status, stream)
+        ref = torch.from_numpy(np.concatenate([t.reshape(-1) for t in tensors]).view(np.int16))
+        exact &= torch.equal(out[: hs.n_weights].view(torch.int16).cpu(), ref)
+    exact &= int(status.item()) == 0
+    blocks = lat[:, [i for i, u in enumerate(units) if u[0].name.startswith("block")]]
+    avg_pass_ms = float(lat.sum(axis=1).mean())
+    achieved = alg / (avg_pass_ms * 1e-3) / 1e9
+    line = {
+        "metric": "decompressed BF16 GB/s",
+        "value": round(2 * n_total * passes / wall / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": passes, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / passes, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "n_weights": n_total, "units": len(units),
+            "layout": f"T256xB{args.bpt}", "bit_exact": bool(exact),
+            "unit_ms_p50": round(float(np.percentile(lat, 50)), 4),
+            "unit_ms_p99": round(float(np.percentile(lat, 99)), 4),
+            "block_ms_p50": round(float(np.percentile(blocks, 50)), 4) if blocks.size else None,
+            "block_ms_p99": round(float(np.percentile(blocks, 99)), 4) if blocks.size else None,
+            "per_unit_ms_mean": {u[0].name: round(float(lat[:, i].mean()), 4)
+                                 for i, u in enumerate(units)},
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+    if not exact:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

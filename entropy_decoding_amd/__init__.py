@@ -1,0 +1,338 @@
+"""Python binding of libdf11 (DFloat11-style lossless BF16 compression on MI355X).
+
+Argument marshalling only: every step of compression runs in the library's
+C++ host code and every step of decompression in its HIP kernels.  PyTorch is
+used for device memory and streams (``tensor.data_ptr()``,
+``torch.cuda.current_stream().cuda_stream``).  The functions keep the C names:
+``df11_build_codebook``, ``df11_encode_size``, ``df11_encode``,
+``df11_decompress_block``, ``df11_decompress_tensor``.
+
+The library must be built (``entropy_decoding_amd.build.build_library()``);
+importing this module without it raises ImportError.  There is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdf11.so")
+
+DF11_MAX_CODE_LEN = 32
+DF11_MAX_LUTS = 64
+DF11_STREAM_PAD = 16
+
+DF11_OK = 0
+DF11_E_INVALID = 1
+DF11_E_LUT_BUDGET = 2
+DF11_E_SYMBOL = 3
+DF11_E_CAPACITY = 4
+DF11_E_HIP = 5
+DF11_E_CORRUPT = 6
+
+DEFAULT_THREADS = 256
+DEFAULT_BYTES_PER_THREAD = 8
+
+
+class Df11Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+
+
+class df11_codebook(ctypes.Structure):
+    _fields_ = [
+        ("code_len", ctypes.c_uint8 * 256),
+        ("code", ctypes.c_uint32 * 256),
+        ("n_luts", ctypes.c_uint32),
+        ("max_len", ctypes.c_uint32),
+        ("lut", (ctypes.c_uint16 * 256) * DF11_MAX_LUTS),
+    ]
+
+
+class df11_sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "n_weights", "total_bits", "n_tiles", "n_windows", "stream_bytes", "sm_bytes",
+        "bop_entries")]
+
+
+class df11_host_stream(ctypes.Structure):
+    _fields_ = [
+        ("stream", _u8p),
+        ("sm", _u8p),
+        ("gaps", _u8p),
+        ("block_out_pos", _u32p),
+        ("tensor_offsets", _u64p),
+        ("tensor_tiles", _u64p),
+        ("stream_capacity", ctypes.c_uint64),
+        ("sm_capacity", ctypes.c_uint64),
+        ("gaps_capacity", ctypes.c_uint64),
+        ("bop_capacity", ctypes.c_uint64),
+        ("n_tensors", ctypes.c_uint32),
+        ("threads", ctypes.c_uint32),
+        ("bytes_per_thread", ctypes.c_uint32),
+        ("max_tile_symbols", ctypes.c_uint32),
+        ("n_weights", ctypes.c_uint64),
+        ("total_bits", ctypes.c_uint64),
+        ("n_tiles", ctypes.c_uint64),
+    ]
+
+
+class df11_device_stream(ctypes.Structure):
+    _fields_ = [
+        ("stream", ctypes.c_void_p),
+        ("sm", ctypes.c_void_p),
+        ("gaps", ctypes.c_void_p),
+        ("block_out_pos", ctypes.c_void_p),
+        ("lut", ctypes.c_void_p),
+        ("tensor_offsets", _u64p),
+        ("tensor_tiles", _u64p),
+        ("n_weights", ctypes.c_uint64),
+        ("total_bits", ctypes.c_uint64),
+        ("n_tiles", ctypes.c_uint64),
+        ("n_luts", ctypes.c_uint32),
+        ("threads", ctypes.c_uint32),
+        ("bytes_per_thread", ctypes.c_uint32),
+        ("max_tile_symbols", ctypes.c_uint32),
+        ("n_tensors", ctypes.c_uint32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run entropy_decoding_amd.build.build_library()")
+    # PyTorch ships its own libamdhip64 (soname libamdhip64.so.7).  Loading torch
+    # first lets the dynamic loader satisfy libdf11's dependency with that same
+    # runtime; loading libdf11 first would bring in a second HIP runtime, whose
+    # streams and launches are invisible to torch's.
+    import torch  # noqa: F401
+
+    L = ctypes.CDLL(LIB_PATH)
+    tens = ctypes.POINTER(_u16p)
+    L.df11_build_codebook.argtypes = [tens, _u64p, ctypes.c_uint32, ctypes.POINTER(df11_codebook)]
+    L.df11_encode_size.argtypes = [ctypes.POINTER(df11_codebook), tens, _u64p, ctypes.c_uint32,
+                                   ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(df11_sizes)]
+    L.df11_encode.argtypes = [ctypes.POINTER(df11_codebook), tens, _u64p, ctypes.c_uint32,
+                              ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(df11_host_stream)]
+    L.df11_decompress_block.argtypes = [ctypes.POINTER(df11_device_stream), ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    L.df11_decompress_tensor.argtypes = [ctypes.POINTER(df11_device_stream), ctypes.c_uint32,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.df11_status_string.argtypes = [ctypes.c_int]
+    L.df11_status_string.restype = ctypes.c_char_p
+    for f in (L.df11_build_codebook, L.df11_encode_size, L.df11_encode,
+              L.df11_decompress_block, L.df11_decompress_tensor):
+        f.restype = ctypes.c_int
+    return L
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.df11_status_string(int(status)).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != DF11_OK:
+        raise Df11Error(fn, rc)
+
+
+def _tensor_args(tensors):
+    if isinstance(tensors, np.ndarray):
+        tensors = [tensors]
+    arrs = []
+    for t in tensors:
+        a = np.asarray(t)
+        if a.dtype != np.uint16:
+            raise TypeError("tensors must be uint16 BF16 bit patterns")
+        arrs.append(np.ascontiguousarray(a).reshape(-1))
+    n = len(arrs)
+    ptrs = (_u16p * max(n, 1))(*[a.ctypes.data_as(_u16p) for a in arrs])
+    numel = (ctypes.c_uint64 * max(n, 1))(*[a.size for a in arrs])
+    return arrs, ptrs, numel, n
+
+
+# ---------------------------------------------------------------- host calls
+
+
+def df11_build_codebook(tensors) -> df11_codebook:
+    """Histogram + Huffman (+ package-merge at 32 bits) + canonical codes + LUTs."""
+    arrs, ptrs, numel, n = _tensor_args(tensors)
+    cb = df11_codebook()
+    _check("df11_build_codebook", LIB.df11_build_codebook(ptrs, numel, n, ctypes.byref(cb)))
+    return cb
+
+
+def df11_encode_size(cb: df11_codebook, tensors, threads: int = DEFAULT_THREADS,
+                     bytes_per_thread: int = DEFAULT_BYTES_PER_THREAD) -> df11_sizes:
+    arrs, ptrs, numel, n = _tensor_args(tensors)
+    sz = df11_sizes()
+    _check("df11_encode_size", LIB.df11_encode_size(ctypes.byref(cb), ptrs, numel, n, threads,
+                                                    bytes_per_thread, ctypes.byref(sz)))
+    return sz
+
+
+@dataclass
+class HostStream:
+    """A compressed unit in host memory (numpy arrays owned by this object)."""
+
+    stream: np.ndarray
+    sm: np.ndarray
+    gaps: np.ndarray
+    block_out_pos: np.ndarray
+    tensor_offsets: np.ndarray
+    tensor_tiles: np.ndarray
+    threads: int
+    bytes_per_thread: int
+    max_tile_symbols: int
+    n_weights: int
+    total_bits: int
+    n_tiles: int
+
+    @property
+    def n_tensors(self) -> int:
+        return self.tensor_offsets.size - 1
+
+    def compressed_bytes(self, cb: df11_codebook | None = None) -> dict:
+        """Bytes of every array a decompression reads (payload and auxiliary)."""
+        d = {
+            "stream": (self.total_bits + 7) // 8,
+            "sm": self.n_weights,
+            "gaps": self.gaps.size,
+            "block_out_pos": 4 * self.block_out_pos.size,
+        }
+        if cb is not None:
+            d["lut"] = 512 * cb.n_luts
+        return d
+
+
+def df11_encode(cb: df11_codebook, tensors, threads: int = DEFAULT_THREADS,
+                bytes_per_thread: int = DEFAULT_BYTES_PER_THREAD) -> HostStream:
+    arrs, ptrs, numel, n = _tensor_args(tensors)
+    sz = df11_encode_size(cb, arrs, threads, bytes_per_thread)
+    stream = np.empty(sz.stream_bytes, dtype=np.uint8)
+    sm = np.empty(sz.sm_bytes, dtype=np.uint8)
+    gaps = np.empty(max(1, sz.n_windows), dtype=np.uint8)
+    bop = np.empty(sz.bop_entries, dtype=np.uint32)
+    offs = np.empty(n + 1, dtype=np.uint64)
+    tiles = np.empty(max(1, 2 * n), dtype=np.uint64)
+    hs = df11_host_stream()
+    hs.stream = stream.ctypes.data_as(_u8p)
+    hs.sm = sm.ctypes.data_as(_u8p)
+    hs.gaps = gaps.ctypes.data_as(_u8p)
+    hs.block_out_pos = bop.ctypes.data_as(_u32p)
+    hs.tensor_offsets = offs.ctypes.data_as(_u64p)
+    hs.tensor_tiles = tiles.ctypes.data_as(_u64p)
+    hs.stream_capacity = stream.size
+    hs.sm_capacity = sm.size
+    hs.gaps_capacity = sz.n_windows
+    hs.bop_capacity = bop.size
+    hs.n_tensors = n
+    _check("df11_encode", LIB.df11_encode(ctypes.byref(cb), ptrs, numel, n, threads,
+                                          bytes_per_thread, ctypes.byref(hs)))
+    return HostStream(stream, sm, gaps[: sz.n_windows], bop, offs, tiles[: 2 * n],
+                      hs.threads, hs.bytes_per_thread, hs.max_tile_symbols, hs.n_weights,
+                      hs.total_bits, hs.n_tiles)
+
+
+# ---------------------------------------------------------------- device side
+
+
+class DeviceStream:
+    """A compressed unit resident in device memory (torch uint8/int32 tensors).
+
+    Holds the ctypes descriptor passed to df11_decompress_*; the host-side
+    tensor metadata (offsets, tile ranges) stays in numpy arrays it owns.
+    """
+
+    def __init__(self, hs: HostStream, cb: df11_codebook, device="cuda"):
+        import torch
+
+        def up(a):
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1))
+            return t.to(device)
+
+        self.host = hs
+        self.stream = up(hs.stream)
+        self.sm = up(hs.sm)
+        self.gaps = up(hs.gaps if hs.gaps.size else np.zeros(1, np.uint8))
+        self.block_out_pos = up(hs.block_out_pos)
+        lut = np.ctypeslib.as_array(cb.lut).reshape(-1)[: 256 * cb.n_luts].copy()
+        self.lut = up(lut)
+        self.tensor_offsets = np.ascontiguousarray(hs.tensor_offsets, dtype=np.uint64)
+        self.tensor_tiles = np.ascontiguousarray(
+            hs.tensor_tiles if hs.tensor_tiles.size else np.zeros(2, np.uint64), dtype=np.uint64)
+        d = df11_device_stream()
+        d.stream = self.stream.data_ptr()
+        d.sm = self.sm.data_ptr()
+        d.gaps = self.gaps.data_ptr()
+        d.block_out_pos = self.block_out_pos.data_ptr()
+        d.lut = self.lut.data_ptr()
+        d.tensor_offsets = self.tensor_offsets.ctypes.data_as(_u64p)
+        d.tensor_tiles = self.tensor_tiles.ctypes.data_as(_u64p)
+        d.n_weights = hs.n_weights
+        d.total_bits = hs.total_bits
+        d.n_tiles = hs.n_tiles
+        d.n_luts = cb.n_luts
+        d.threads = hs.threads
+        d.bytes_per_thread = hs.bytes_per_thread
+        d.max_tile_symbols = hs.max_tile_symbols
+        d.n_tensors = hs.n_tensors
+        self.desc = d
+
+    @property
+    def n_weights(self) -> int:
+        return int(self.desc.n_weights)
+
+    def device_bytes(self) -> int:
+        return sum(t.numel() for t in (self.stream, self.sm, self.gaps, self.block_out_pos,
+                                       self.lut))
+
+
+def _stream_handle(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def df11_decompress_block(ds: DeviceStream, out, status=None, stream=None) -> None:
+    """One launch decompressing the whole unit into ``out`` (a device tensor of
+    n_weights 16-bit elements, e.g. torch.bfloat16 or torch.int16)."""
+    if out.numel() < ds.n_weights or out.element_size() != 2 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous 16-bit device tensor of n_weights elements")
+    sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
+    _check("df11_decompress_block",
+           LIB.df11_decompress_block(ctypes.byref(ds.desc), ctypes.c_void_p(out.data_ptr()), sp,
+                                     _stream_handle(stream)))
+
+
+def df11_decompress_tensor(ds: DeviceStream, k: int, out, status=None, stream=None) -> None:
+    """Decompress tensor k of the unit into ``out`` (its numel 16-bit elements)."""
+    n = 0
+    if 0 <= k < ds.tensor_offsets.size - 1:
+        n = int(ds.tensor_offsets[k + 1] - ds.tensor_offsets[k])
+    if out.numel() < n or out.element_size() != 2 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous 16-bit device tensor of the tensor's numel")
+    sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
+    _check("df11_decompress_tensor",
+           LIB.df11_decompress_tensor(ctypes.byref(ds.desc), int(k),
+                                      ctypes.c_void_p(out.data_ptr()), sp,
+                                      _stream_handle(stream)))
+
+
+def codebook_arrays(cb: df11_codebook):
+    """(code_len uint8[256], code uint32[256]) views of a codebook."""
+    return (np.ctypeslib.as_array(cb.code_len).copy(), np.ctypeslib.as_array(cb.code).copy())

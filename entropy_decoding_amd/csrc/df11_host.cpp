@@ -1,0 +1,504 @@
+// Host half of the DFloat11-style codec: codebook construction and the
+// offline encoder ("70% Size, 100% Accuracy ... (DFloat11)", abstract:
+// frequency-based dynamic-length codes; "Compressing LLMs without
+// Compromise", "Three ways to spend the savings": exponents are
+// Huffman-coded offline).  Stream format and ABI: include/df11.h.
+#include "df11.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <exception>
+#include <thread>
+#include <vector>
+
+namespace {
+
+constexpr int kSyms = 256;
+constexpr uint64_t kChunk = uint64_t(1) << 22;  // weights per encoder work item
+
+unsigned worker_count() {
+    if (const char *e = std::getenv("DF11_HOST_THREADS")) {
+        int v = std::atoi(e);
+        if (v > 0) return unsigned(v);
+    }
+    unsigned hc = std::thread::hardware_concurrency();
+    return std::max(1u, std::min(16u, hc ? hc : 1u));
+}
+
+// Runs f(i) for i in [0, n) on up to worker_count() threads.
+template <class F>
+void parallel_for(size_t n, F &&f) {
+    size_t nt = std::min<size_t>(n, worker_count());
+    if (nt <= 1) {
+        for (size_t i = 0; i < n; i++) f(i);
+        return;
+    }
+    std::atomic<size_t> next{0};
+    auto body = [&] {
+        for (size_t i; (i = next.fetch_add(1, std::memory_order_relaxed)) < n;) f(i);
+    };
+    std::vector<std::thread> pool;
+    pool.reserve(nt - 1);
+    for (size_t t = 0; t + 1 < nt; t++) pool.emplace_back(body);
+    body();
+    for (auto &th : pool) th.join();
+}
+
+struct Piece {
+    const uint16_t *w;
+    uint64_t count;
+    uint64_t begin;  // global weight index
+    uint32_t tensor;
+};
+
+std::vector<Piece> split(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n) {
+    std::vector<Piece> out;
+    uint64_t g = 0;
+    for (uint32_t k = 0; k < n; k++) {
+        for (uint64_t o = 0; o < numel[k]; o += kChunk)
+            out.push_back({tensors[k] + o, std::min(kChunk, numel[k] - o), g + o, k});
+        g += numel[k];
+    }
+    return out;
+}
+
+// Exponent histogram over all pieces, one partial table per piece.
+void histogram(const std::vector<Piece> &pieces, std::vector<uint64_t> &per_piece,
+               uint64_t total[kSyms]) {
+    per_piece.assign(pieces.size() * kSyms, 0);
+    parallel_for(pieces.size(), [&](size_t p) {
+        uint32_t h[4][kSyms] = {};
+        const uint16_t *w = pieces[p].w;
+        uint64_t n = pieces[p].count, i = 0;
+        for (; i + 4 <= n; i += 4) {
+            h[0][(w[i] >> 7) & 0xFF]++;
+            h[1][(w[i + 1] >> 7) & 0xFF]++;
+            h[2][(w[i + 2] >> 7) & 0xFF]++;
+            h[3][(w[i + 3] >> 7) & 0xFF]++;
+        }
+        for (; i < n; i++) h[0][(w[i] >> 7) & 0xFF]++;
+        uint64_t *dst = &per_piece[p * kSyms];
+        for (int s = 0; s < kSyms; s++) dst[s] = uint64_t(h[0][s]) + h[1][s] + h[2][s] + h[3][s];
+    });
+    std::fill(total, total + kSyms, 0);
+    for (size_t p = 0; p < pieces.size(); p++)
+        for (int s = 0; s < kSyms; s++) total[s] += per_piece[p * kSyms + s];
+}
+
+// ---------------------------------------------------------------- lengths
+
+// Huffman lengths with a binary min-heap on (weight, tiebreak).
+int huffman(const uint64_t counts[kSyms], uint8_t len[kSyms]) {
+    struct Key {
+        uint64_t w;
+        uint32_t tb;
+        int node;
+    };
+    auto greater = [](const Key &a, const Key &b) {
+        return a.w != b.w ? a.w > b.w : a.tb > b.tb;
+    };
+    std::vector<Key> heap;
+    int parent[2 * kSyms];
+    int leaf_node[kSyms];
+    int nodes = 0;
+    std::memset(len, 0, kSyms);
+    for (int s = 0; s < kSyms; s++) {
+        leaf_node[s] = -1;
+        if (counts[s]) {
+            leaf_node[s] = nodes;
+            parent[nodes] = -1;
+            heap.push_back({counts[s], uint32_t(s), nodes++});
+        }
+    }
+    const int present = nodes;
+    if (present == 0) return 0;
+    if (present == 1) {
+        int only = 0, dummy = 0;
+        while (!counts[only]) only++;
+        while (counts[dummy]) dummy++;
+        len[only] = len[dummy] = 1;
+        return 1;
+    }
+    std::make_heap(heap.begin(), heap.end(), greater);
+    for (int k = 0; k + 1 < present; k++) {
+        std::pop_heap(heap.begin(), heap.end(), greater);
+        Key a = heap.back();
+        heap.pop_back();
+        std::pop_heap(heap.begin(), heap.end(), greater);
+        Key b = heap.back();
+        heap.pop_back();
+        parent[a.node] = parent[b.node] = nodes;
+        parent[nodes] = -1;
+        heap.push_back({a.w + b.w, uint32_t(kSyms + k), nodes++});
+        std::push_heap(heap.begin(), heap.end(), greater);
+    }
+    // depth of node v = depth(parent) + 1; parents are created after children,
+    // so walking node ids downward from the root visits parents first
+    std::vector<int> depth(nodes, 0);
+    for (int v = nodes - 2; v >= 0; v--) depth[v] = depth[parent[v]] + 1;
+    int mx = 0;
+    for (int s = 0; s < kSyms; s++)
+        if (leaf_node[s] >= 0) {
+            len[s] = uint8_t(std::min(depth[leaf_node[s]], 255));
+            mx = std::max(mx, depth[leaf_node[s]]);
+        }
+    return mx;
+}
+
+// Length-limited optimal lengths by package-merge.  Uses the prefix property:
+// the items chosen from every denomination list form a prefix of it, so only
+// the number of packages inside each chosen prefix is needed.
+int package_merge(const uint64_t counts[kSyms], int limit, uint8_t len[kSyms]) {
+    std::vector<int> sym;
+    for (int s = 0; s < kSyms; s++)
+        if (counts[s]) sym.push_back(s);
+    const size_t n = sym.size();
+    std::stable_sort(sym.begin(), sym.end(),
+                     [&](int a, int b) { return counts[a] < counts[b]; });
+    std::memset(len, 0, kSyms);
+    // lists[l]: weights and package flags for denomination 2^-l, l = 1..limit
+    std::vector<std::vector<uint64_t>> wt(limit + 1);
+    std::vector<std::vector<uint8_t>> pkg(limit + 1);
+    for (size_t i = 0; i < n; i++) {
+        wt[limit].push_back(counts[sym[i]]);
+        pkg[limit].push_back(0);
+    }
+    for (int l = limit - 1; l >= 1; l--) {
+        const auto &below = wt[l + 1];
+        size_t np = below.size() / 2, li = 0, pi = 0;
+        while (li < n || pi < np) {
+            uint64_t pw = pi < np ? below[2 * pi] + below[2 * pi + 1] : 0;
+            if (li < n && (pi >= np || counts[sym[li]] <= pw)) {
+                wt[l].push_back(counts[sym[li++]]);
+                pkg[l].push_back(0);
+            } else {
+                wt[l].push_back(pw);
+                pkg[l].push_back(1);
+                pi++;
+            }
+        }
+    }
+    size_t take = 2 * n - 2;
+    int mx = 0;
+    for (int l = 1; l <= limit && take; l++) {
+        size_t packages = 0;
+        for (size_t i = 0; i < take; i++) packages += pkg[l][i];
+        size_t leaves = take - packages;  // the cheapest `leaves` symbols get one more bit
+        for (size_t i = 0; i < leaves; i++) {
+            len[sym[i]]++;
+            mx = std::max<int>(mx, len[sym[i]]);
+        }
+        take = 2 * packages;
+    }
+    return mx;
+}
+
+// Canonical codes from lengths: per-length counts give each length's first
+// code; symbols of equal length take consecutive codes in value order.
+void canonical(const uint8_t len[kSyms], uint32_t code[kSyms]) {
+    uint64_t count[DF11_MAX_CODE_LEN + 2] = {}, next[DF11_MAX_CODE_LEN + 2] = {};
+    for (int s = 0; s < kSyms; s++)
+        if (len[s]) count[len[s]]++;
+    for (int l = 2; l <= DF11_MAX_CODE_LEN; l++) next[l] = (next[l - 1] + count[l - 1]) << 1;
+    for (int s = 0; s < kSyms; s++) code[s] = len[s] ? uint32_t(next[len[s]]++) : 0;
+}
+
+// Hierarchical 8-bit-indexed lookup tables (the compact hierarchical LUTs of
+// the DFloat11 abstract).  A code of length l, left-aligned in 32 bits, is
+// resolved at level floor((l - 1) / 8); shorter levels hold pointers.
+int build_luts(df11_codebook *cb) {
+    std::memset(cb->lut, 0, sizeof(cb->lut));
+    uint32_t n_luts = 1;
+    for (int s = 0; s < kSyms; s++) {
+        const int l = cb->code_len[s];
+        if (!l) continue;
+        const uint32_t v = cb->code[s] << (32 - l);  // l >= 1
+        uint32_t table = 0;
+        for (int lvl = 0;; lvl++) {
+            const uint32_t idx = (v >> (24 - 8 * lvl)) & 0xFF;
+            if (l <= 8 * (lvl + 1)) {
+                const uint32_t span = 1u << (8 * (lvl + 1) - l);
+                for (uint32_t i = 0; i < span; i++)
+                    cb->lut[table][idx + i] = uint16_t((l << 8) | s);
+                break;
+            }
+            uint16_t &e = cb->lut[table][idx];
+            if (!(e & 0x8000)) {
+                if (n_luts >= DF11_MAX_LUTS) return DF11_E_LUT_BUDGET;
+                e = uint16_t(0x8000 | n_luts++);
+            }
+            table = e & 0x7FFF;
+        }
+    }
+    cb->n_luts = n_luts;
+    return DF11_OK;
+}
+
+bool valid_layout(uint32_t T, uint32_t B) { return T == 256 && (B == 8 || B == 16); }
+
+int log2u(uint64_t x) {
+    int r = 0;
+    while ((uint64_t(1) << r) < x) r++;
+    return r;
+}
+
+bool valid_codebook(const df11_codebook *cb) {
+    if (cb->n_luts < 1 || cb->n_luts > DF11_MAX_LUTS) return false;
+    for (int s = 0; s < kSyms; s++)
+        if (cb->code_len[s] > DF11_MAX_CODE_LEN) return false;
+    return true;
+}
+
+int sizes_from_counts(const df11_codebook *cb, const uint64_t counts[kSyms], uint64_t n,
+                      uint32_t T, uint32_t B, df11_sizes *out) {
+    uint64_t bits = 0;
+    for (int s = 0; s < kSyms; s++) {
+        if (counts[s] && !cb->code_len[s]) return DF11_E_SYMBOL;
+        bits += counts[s] * cb->code_len[s];
+    }
+    const uint64_t tile_bits = uint64_t(8) * B * T;
+    out->n_weights = n;
+    out->total_bits = bits;
+    out->n_tiles = (bits + tile_bits - 1) / tile_bits;
+    out->n_windows = out->n_tiles * T;
+    out->stream_bytes = out->n_tiles * T * B + DF11_STREAM_PAD;
+    out->sm_bytes = (n + 63) / 64 * 64 + 64;
+    out->bop_entries = out->n_tiles + 1;
+    return DF11_OK;
+}
+
+bool bad_inputs(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n) {
+    if (n && (!tensors || !numel)) return true;
+    for (uint32_t k = 0; k < n; k++)
+        if (numel[k] && !tensors[k]) return true;
+    return false;
+}
+
+// Per-piece encoder results needed to stitch neighbouring pieces together.
+struct PieceOut {
+    uint64_t first_window = 0, last_window = 0;
+    uint32_t first_gap = 0;
+};
+
+inline void or_byte(uint8_t *p, uint8_t v) {
+    if (v) __atomic_fetch_or(p, v, __ATOMIC_RELAXED);
+}
+
+// Encodes one piece whose first code starts at bit `pos`.
+void encode_piece(const df11_codebook *cb, const Piece &pc, uint64_t pos, uint64_t end_pos,
+                  int wshift, int tshift, uint8_t *stream, uint8_t *sm, uint8_t *gaps,
+                  uint32_t *bop, PieceOut &po) {
+    const uint64_t wmask = (uint64_t(1) << wshift) - 1;
+    uint64_t byte = pos >> 3;
+    unsigned nacc = unsigned(pos & 7);  // pending bits; the leading ones belong to the previous piece
+    uint64_t acc = 0;
+    bool shared_head = nacc != 0;
+
+    po.first_window = pos >> wshift;
+    po.first_gap = uint32_t(pos & wmask);
+    uint64_t next_window = (po.first_window + 1) << wshift;
+    uint64_t last_window = po.first_window;
+    uint64_t next_tile = ((pos >> tshift) + 1) << tshift;
+
+    const uint16_t *w = pc.w;
+    uint8_t *smo = sm + pc.begin;
+    for (uint64_t i = 0; i < pc.count; i++) {
+        const uint32_t x = w[i];
+        const uint32_t e = (x >> 7) & 0xFF;
+        if (pos >= next_window) {  // first code starting in a new window
+            last_window = pos >> wshift;
+            gaps[last_window] = uint8_t(pos & wmask);
+            next_window = (last_window + 1) << wshift;
+        }
+        if (pos >= next_tile) {  // first code at or after a tile boundary
+            bop[next_tile >> tshift] = uint32_t(pc.begin + i);
+            next_tile += uint64_t(1) << tshift;
+        }
+        const unsigned l = cb->code_len[e];
+        acc = (acc << l) | cb->code[e];
+        nacc += l;
+        pos += l;
+        if (nacc >= 32) {
+            const uint32_t word = uint32_t(acc >> (nacc - 32));
+            uint8_t b[4] = {uint8_t(word >> 24), uint8_t(word >> 16), uint8_t(word >> 8),
+                            uint8_t(word)};
+            if (shared_head) {
+                or_byte(stream + byte, b[0]);
+                std::memcpy(stream + byte + 1, b + 1, 3);
+                shared_head = false;
+            } else {
+                std::memcpy(stream + byte, b, 4);
+            }
+            byte += 4;
+            nacc -= 32;
+            acc &= (uint64_t(1) << nacc) - 1;
+        }
+        smo[i] = uint8_t(((x >> 8) & 0x80) | (x & 0x7F));
+    }
+    // tail bytes, the last possibly shared with the next piece
+    for (unsigned k = 0; k < nacc; k += 8) {
+        const unsigned take = std::min(8u, nacc - k);
+        const uint8_t v = uint8_t(((acc >> (nacc - k - take)) & ((1u << take) - 1)) << (8 - take));
+        or_byte(stream + byte++, v);
+    }
+    // tile boundaries after this piece's last code start, up to the next piece's first
+    while (next_tile <= end_pos) {
+        bop[next_tile >> tshift] = uint32_t(pc.begin + pc.count);
+        next_tile += uint64_t(1) << tshift;
+    }
+    po.last_window = last_window;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *df11_status_string(int status) {
+    switch (status) {
+    case DF11_OK: return "ok";
+    case DF11_E_INVALID: return "invalid argument";
+    case DF11_E_LUT_BUDGET: return "codebook needs more lookup tables than DF11_MAX_LUTS";
+    case DF11_E_SYMBOL: return "input exponent has no code in the codebook";
+    case DF11_E_CAPACITY: return "output buffer smaller than df11_encode_size reports";
+    case DF11_E_HIP: return "HIP launch error";
+    case DF11_E_CORRUPT: return "compressed stream is inconsistent with its auxiliary arrays";
+    default: return "unknown status";
+    }
+}
+
+int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n_tensors,
+                        df11_codebook *cb) {
+    try {
+        if (!cb || bad_inputs(tensors, numel, n_tensors)) return DF11_E_INVALID;
+        auto pieces = split(tensors, numel, n_tensors);
+        std::vector<uint64_t> per;
+        uint64_t counts[kSyms];
+        histogram(pieces, per, counts);
+        uint64_t n = 0;
+        for (int s = 0; s < kSyms; s++) n += counts[s];
+        if (n == 0) return DF11_E_INVALID;
+        std::memset(cb, 0, sizeof(*cb));
+        int mx = huffman(counts, cb->code_len);
+        if (mx > DF11_MAX_CODE_LEN) mx = package_merge(counts, DF11_MAX_CODE_LEN, cb->code_len);
+        cb->max_len = uint32_t(mx);
+        canonical(cb->code_len, cb->code);
+        return build_luts(cb);
+    } catch (...) {
+        return DF11_E_INVALID;
+    }
+}
+
+int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors, const uint64_t *numel,
+                     uint32_t n_tensors, uint32_t threads, uint32_t bytes_per_thread,
+                     df11_sizes *out) {
+    try {
+        if (!cb || !out || bad_inputs(tensors, numel, n_tensors) ||
+            !valid_layout(threads, bytes_per_thread) || !valid_codebook(cb))
+            return DF11_E_INVALID;
+        auto pieces = split(tensors, numel, n_tensors);
+        std::vector<uint64_t> per;
+        uint64_t counts[kSyms];
+        histogram(pieces, per, counts);
+        uint64_t n = 0;
+        for (uint32_t k = 0; k < n_tensors; k++) n += numel[k];
+        return sizes_from_counts(cb, counts, n, threads, bytes_per_thread, out);
+    } catch (...) {
+        return DF11_E_INVALID;
+    }
+}
+
+int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const uint64_t *numel,
+                uint32_t n_tensors, uint32_t threads, uint32_t bytes_per_thread,
+                df11_host_stream *out) {
+    try {
+        if (!cb || !out || bad_inputs(tensors, numel, n_tensors) ||
+            !valid_layout(threads, bytes_per_thread) || !valid_codebook(cb) ||
+            out->n_tensors != n_tensors)
+            return DF11_E_INVALID;
+        auto pieces = split(tensors, numel, n_tensors);
+        std::vector<uint64_t> per;
+        uint64_t counts[kSyms];
+        histogram(pieces, per, counts);
+        uint64_t n = 0;
+        for (uint32_t k = 0; k < n_tensors; k++) n += numel[k];
+        if (n >= (uint64_t(1) << 32)) return DF11_E_INVALID;
+        df11_sizes sz;
+        int rc = sizes_from_counts(cb, counts, n, threads, bytes_per_thread, &sz);
+        if (rc != DF11_OK) return rc;
+        if (!out->stream || !out->sm || !out->block_out_pos || !out->tensor_offsets ||
+            (n_tensors && !out->tensor_tiles) || (sz.n_windows && !out->gaps))
+            return DF11_E_INVALID;
+        if (out->stream_capacity < sz.stream_bytes || out->sm_capacity < sz.sm_bytes ||
+            out->gaps_capacity < sz.n_windows || out->bop_capacity < sz.bop_entries)
+            return DF11_E_CAPACITY;
+
+        // start bit of every piece
+        std::vector<uint64_t> start(pieces.size() + 1, 0);
+        for (size_t p = 0; p < pieces.size(); p++) {
+            uint64_t b = 0;
+            for (int s = 0; s < kSyms; s++) b += per[p * kSyms + s] * cb->code_len[s];
+            start[p + 1] = start[p] + b;
+        }
+        const int wshift = log2u(uint64_t(8) * bytes_per_thread);
+        const int tshift = wshift + log2u(threads);
+
+        std::memset(out->stream, 0, sz.stream_bytes);
+        std::memset(out->gaps, 255, sz.n_windows);
+        std::memset(out->sm + n, 0, sz.sm_bytes - n);
+        out->block_out_pos[0] = 0;
+        out->block_out_pos[sz.n_tiles] = uint32_t(n);
+
+        std::vector<PieceOut> po(pieces.size());
+        parallel_for(pieces.size(), [&](size_t p) {
+            encode_piece(cb, pieces[p], start[p], start[p + 1], wshift, tshift, out->stream,
+                         out->sm, out->gaps, out->block_out_pos, po[p]);
+        });
+        // a piece's first window may already have a code start from the piece before
+        bool have_prev = false;
+        uint64_t prev_last = 0;
+        for (size_t p = 0; p < pieces.size(); p++) {
+            if (!pieces[p].count) continue;
+            if (!have_prev || prev_last != po[p].first_window)
+                out->gaps[po[p].first_window] = uint8_t(po[p].first_gap);
+            have_prev = true;
+            prev_last = po[p].last_window;
+        }
+
+        // per-tensor element offsets and tile ranges
+        uint64_t g = 0, bit = 0;
+        for (uint32_t k = 0; k < n_tensors; k++) {
+            out->tensor_offsets[k] = g;
+            uint64_t bits_k = 0;
+            for (size_t p = 0; p < pieces.size(); p++)
+                if (pieces[p].tensor == k) bits_k += start[p + 1] - start[p];
+            out->tensor_tiles[2 * k] = bit >> tshift;
+            if (numel[k]) {
+                const uint16_t last = tensors[k][numel[k] - 1];
+                const uint64_t last_start = bit + bits_k - cb->code_len[(last >> 7) & 0xFF];
+                out->tensor_tiles[2 * k + 1] = (last_start >> tshift) + 1;
+            } else {
+                out->tensor_tiles[2 * k + 1] = out->tensor_tiles[2 * k];
+            }
+            g += numel[k];
+            bit += bits_k;
+        }
+        out->tensor_offsets[n_tensors] = n;
+
+        uint32_t mx = 0;
+        for (uint64_t t = 0; t < sz.n_tiles; t++)
+            mx = std::max(mx, out->block_out_pos[t + 1] - out->block_out_pos[t]);
+        out->threads = threads;
+        out->bytes_per_thread = bytes_per_thread;
+        out->max_tile_symbols = mx;
+        out->n_weights = n;
+        out->total_bits = sz.total_bits;
+        out->n_tiles = sz.n_tiles;
+        return DF11_OK;
+    } catch (...) {
+        return DF11_E_INVALID;
+    }
+}
+
+}  // extern "C"

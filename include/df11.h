@@ -1,0 +1,211 @@
+/*
+ * df11.h -- C ABI of an MI355X (gfx950) library for DFloat11-style lossless
+ * BF16 weight compression.
+ *
+ * Method: "70% Size, 100% Accuracy: Lossless LLM Compression for Efficient GPU
+ * Inference via Dynamic-Length Float (DFloat11)", abstract.  Each BF16 weight
+ * keeps its sign and 7 mantissa bits verbatim in one byte; its 8-bit exponent
+ * is replaced by a variable-length code chosen from exponent frequencies; a GPU
+ * kernel restores bit-identical BF16 values using compact hierarchical lookup
+ * tables held in on-chip memory, a two-phase scheme whose small auxiliary
+ * arrays tell each thread where to read and where to write, and one launch
+ * per transformer block.  The BF16 field split (1 sign, 8 exponent, 7
+ * mantissa bits; only the exponent carries low entropy) and offline Huffman
+ * coding of the exponents are from "Compressing LLMs without Compromise",
+ * sections "Where the redundancy lives" and "Three ways to spend the savings".
+ *
+ * Terms used below:
+ *   weight w      uint16 BF16 bit pattern
+ *   exponent e    (w >> 7) & 0xFF, the coded symbol (all 256 values allowed,
+ *                 including those of Inf/NaN and zero/subnormals)
+ *   sm byte       ((w >> 8) & 0x80) | (w & 0x7F), stored raw
+ *   unit          the tensors compressed together under one codebook and
+ *                 decompressed by one launch (a tensor, or all weight tensors
+ *                 of one transformer block, concatenated in order)
+ *   window        B consecutive stream bytes decoded by one GPU thread
+ *   tile          T consecutive windows decoded by one workgroup
+ *
+ * Stream format.  Codes are canonical (symbols ordered by (length, value)
+ * take consecutive codes), at most 32 bits long, and written MSB-first: bit j
+ * of the stream is bit 7 - (j % 8) of byte j / 8.  gaps[j] is the offset, in
+ * bits, of the first code that starts in window j (always < 32), or 255 when
+ * no code starts there.  block_out_pos[t] is the number of codes that start
+ * before tile t, so tile t writes outputs [block_out_pos[t], block_out_pos[t+1]).
+ *
+ * Conventions.  Every call returns a df11_status.  No call allocates device
+ * memory, frees caller memory or synchronises a stream; host calls may use
+ * worker threads internally and are thread-safe (no global mutable state).
+ */
+#ifndef DF11_H
+#define DF11_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DF11_MAX_CODE_LEN 32   /* longest code; 4 levels of 8-bit-indexed tables */
+#define DF11_MAX_LUTS 64       /* table budget: 64 x 256 x 2 B = 32 KiB of LDS */
+#define DF11_STREAM_PAD 16     /* zero bytes after the last window (look-ahead) */
+
+typedef enum df11_status {
+    DF11_OK = 0,
+    DF11_E_INVALID = 1,     /* bad argument: null pointer, size, layout, alignment */
+    DF11_E_LUT_BUDGET = 2,  /* codebook needs more than DF11_MAX_LUTS tables */
+    DF11_E_SYMBOL = 3,      /* an input exponent has no code in the codebook */
+    DF11_E_CAPACITY = 4,    /* a caller buffer is smaller than df11_encode_size says */
+    DF11_E_HIP = 5,         /* the HIP runtime rejected the launch */
+    DF11_E_CORRUPT = 6      /* written to *d_status by the kernel: inconsistent stream */
+} df11_status;
+
+/* An opaque hipStream_t (0 = the null stream). */
+typedef void *df11_hip_stream;
+
+/*
+ * Codebook (caller-owned POD, about 34 KiB).  code_len[s] == 0 means symbol s
+ * has no code.  lut holds n_luts tables of 256 uint16 entries; table 0 is
+ * indexed by the top 8 bits of a 32-bit left-aligned window of the stream,
+ * a level-k table by the next 8 bits.  Entry formats:
+ *   leaf     bit 15 = 0, bits 13..8 = full code length (1..32), bits 7..0 = symbol
+ *   pointer  bit 15 = 1, bits 14..0 = index of the next-level table
+ */
+typedef struct df11_codebook {
+    uint8_t code_len[256];
+    uint32_t code[256];
+    uint32_t n_luts;
+    uint32_t max_len;
+    uint16_t lut[DF11_MAX_LUTS][256];
+} df11_codebook;
+
+/* Exact sizes of everything df11_encode writes, for caller allocation. */
+typedef struct df11_sizes {
+    uint64_t n_weights;      /* N: weights in the unit */
+    uint64_t total_bits;     /* exponent code bits, sum over weights of code_len[e] */
+    uint64_t n_tiles;        /* ceil(total_bits / (8 * B * T)) */
+    uint64_t n_windows;      /* n_tiles * T: bytes of gaps */
+    uint64_t stream_bytes;   /* n_tiles * T * B + DF11_STREAM_PAD */
+    uint64_t sm_bytes;       /* N rounded up to 64, plus 64 bytes of padding */
+    uint64_t bop_entries;    /* n_tiles + 1 entries of block_out_pos */
+} df11_sizes;
+
+/*
+ * A compressed unit in caller-owned HOST memory, filled by df11_encode.
+ * The caller sets the pointers (and their capacities, from df11_sizes) and
+ * n_tensors; df11_encode fills the arrays and the scalar results.
+ */
+typedef struct df11_host_stream {
+    uint8_t *stream;            /* [stream_bytes] */
+    uint8_t *sm;                /* [sm_bytes]; bytes past N are zero */
+    uint8_t *gaps;              /* [n_windows] */
+    uint32_t *block_out_pos;    /* [n_tiles + 1] */
+    uint64_t *tensor_offsets;   /* [n_tensors + 1] element offset of each tensor, then N */
+    uint64_t *tensor_tiles;     /* [2 * n_tensors] first tile and one-past-last tile per tensor */
+    uint64_t stream_capacity, sm_capacity, gaps_capacity, bop_capacity;
+    uint32_t n_tensors;
+    /* results */
+    uint32_t threads;           /* T */
+    uint32_t bytes_per_thread;  /* B */
+    uint32_t max_tile_symbols;  /* max over tiles of block_out_pos[t+1] - block_out_pos[t] */
+    uint64_t n_weights;
+    uint64_t total_bits;
+    uint64_t n_tiles;
+} df11_host_stream;
+
+/*
+ * A compressed unit in DEVICE memory, as df11_decompress_* read it.  Device
+ * pointers: stream, sm (16-byte aligned), gaps, block_out_pos, lut.  Host
+ * pointers: tensor_offsets and tensor_tiles (read synchronously by
+ * df11_decompress_tensor only; may be null for df11_decompress_block).
+ * Scalars are copied from the df11_host_stream and df11_codebook they came from.
+ */
+typedef struct df11_device_stream {
+    const uint8_t *stream;
+    const uint8_t *sm;
+    const uint8_t *gaps;
+    const uint32_t *block_out_pos;
+    const uint16_t *lut;
+    const uint64_t *tensor_offsets;
+    const uint64_t *tensor_tiles;
+    uint64_t n_weights;
+    uint64_t total_bits;
+    uint64_t n_tiles;
+    uint32_t n_luts;
+    uint32_t threads;
+    uint32_t bytes_per_thread;
+    uint32_t max_tile_symbols;
+    uint32_t n_tensors;
+} df11_device_stream;
+
+/*
+ * df11_build_codebook -- host, offline.
+ * Entropy coding by frequency ("DFloat11" abstract; offline Huffman coding of
+ * exponents, "Three ways to spend the savings").  Counts exponents over all
+ * n_tensors arrays (tensors[k] holds numel[k] weights), builds Huffman code
+ * lengths (ties: smallest (count, tiebreak), leaf tiebreak = symbol value,
+ * k-th merged node = 256 + k; one present symbol is paired with a dummy, the
+ * smallest absent value, both of length 1), limits them to 32 bits by
+ * package-merge when needed, assigns canonical codes, and fills the
+ * hierarchical lookup tables ("compact, hierarchical lookup tables", DFloat11
+ * abstract).  Errors: DF11_E_INVALID (null pointers, no weights at all),
+ * DF11_E_LUT_BUDGET.  *cb is fully overwritten on success.
+ */
+int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel,
+                        uint32_t n_tensors, df11_codebook *cb);
+
+/*
+ * df11_encode_size -- host.  Sizes of all arrays df11_encode will write for
+ * these tensors under layout (threads T, bytes_per_thread B).  Supported
+ * layouts: T = 256 with B = 8 or 16.  Errors: DF11_E_INVALID, DF11_E_SYMBOL.
+ */
+int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors,
+                     const uint64_t *numel, uint32_t n_tensors, uint32_t threads,
+                     uint32_t bytes_per_thread, df11_sizes *out);
+
+/*
+ * df11_encode -- host, offline.  Writes the concatenated exponent code stream,
+ * the sm bytes and the auxiliary arrays (gaps, block_out_pos: the "lightweight
+ * auxiliary variables" that coordinate thread read and write positions,
+ * DFloat11 abstract) into the caller's buffers in *out, plus tensor_offsets
+ * and tensor_tiles.  out->n_tensors must equal n_tensors.  Errors:
+ * DF11_E_INVALID, DF11_E_SYMBOL, DF11_E_CAPACITY (a capacity field below the
+ * df11_encode_size figure), DF11_E_INVALID when N >= 2^32.
+ */
+int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors,
+                const uint64_t *numel, uint32_t n_tensors, uint32_t threads,
+                uint32_t bytes_per_thread, df11_host_stream *out);
+
+/*
+ * df11_decompress_block -- device.  Transformer-block-level decompression
+ * (DFloat11 abstract): the whole unit in exactly one kernel launch, on stream
+ * st, into out[0 .. n_weights) (device memory, 16-byte aligned, caller-owned;
+ * tensor k is out[tensor_offsets[k] .. tensor_offsets[k+1])).  Every output
+ * equals the original BF16 bit pattern.  Asynchronous: returns after the
+ * launch.  Synchronous errors: DF11_E_INVALID (null or misaligned pointers,
+ * unsupported layout, sizes inconsistent with each other), DF11_E_HIP.  The
+ * kernel checks each tile's decoded symbol count against block_out_pos and,
+ * on a mismatch, writes DF11_E_CORRUPT to *d_status (device int32, may be
+ * null) and leaves that tile's outputs unwritten.  N == 0 launches nothing.
+ */
+int df11_decompress_block(const df11_device_stream *s, uint16_t *out, int32_t *d_status,
+                          df11_hip_stream st);
+
+/*
+ * df11_decompress_tensor -- device.  Decompresses only tensor k of the unit
+ * into out[0 .. numel_k) (device, 16-byte aligned) with one launch over the
+ * tiles that hold its codes; same kernel, checks and errors as
+ * df11_decompress_block.  The tensor's element offset in the unit must be a
+ * multiple of 8 (DF11_E_INVALID otherwise; decompress the block instead).
+ */
+int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, uint16_t *out,
+                           int32_t *d_status, df11_hip_stream st);
+
+/* Static description of a status code. */
+const char *df11_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DF11_H */

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP decoder against the oracle and against the original bits.
+
+Every comparison is on 16-bit patterns (int16 views), never on float values.
+Small cases compare every output with the oracle's bit-serial decode; the full
+workloads compare every output with the original tensor (the method is
+lossless: decompressed == original, bit for bit) and sampled tiles with the
+oracle's decode of those tiles.
+"""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import entropy_decoding_amd as ed  # noqa: E402
+import oracle  # noqa: E402
+import synth_weights as sw  # noqa: E402
+
+T = 256
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def _cat(tensors):
+    return np.concatenate([np.asarray(t, dtype=np.uint16).reshape(-1) for t in tensors])
+
+
+def _dev_i16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+class Unit:
+    """Library-compressed unit resident on the GPU."""
+
+    def __init__(self, tensors, bpt=8):
+        self.tensors = [np.asarray(t, dtype=np.uint16).reshape(-1) for t in tensors]
+        self.cb = ed.df11_build_codebook(self.tensors)
+        self.hs = ed.df11_encode(self.cb, self.tensors, T, bpt)
+        self.ds = ed.DeviceStream(self.hs, self.cb, "cuda")
+        self.n = self.hs.n_weights
+        self.bpt = bpt
+
+    def decompress(self, poison=-1, label=""):
+        out = torch.full((max(self.n, 1),), poison, dtype=torch.int16, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        say(f"[gpu] df11_decompress_block {label} N={self.n} tiles={self.hs.n_tiles} "
+            f"B={self.bpt} luts={self.cb.n_luts} max_len={self.cb.max_len}")
+        ed.df11_decompress_block(self.ds, out, status)
+        torch.cuda.synchronize()
+        return out[: self.n], int(status.item())
+
+    def decompress_tensor(self, k, poison=-1, label=""):
+        nk = self.tensors[k].size
+        out = torch.full((max(nk, 1),), poison, dtype=torch.int16, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        say(f"[gpu] df11_decompress_tensor {label} k={k} numel={nk}")
+        ed.df11_decompress_tensor(self.ds, k, out, status)
+        torch.cuda.synchronize()
+        return out[:nk], int(status.item())
+
+    def tile_start_bit(self, t):
+        wb = 8 * self.bpt
+        g = self.hs.gaps[t * T:(t + 1) * T]
+        j = int(np.argmax(g != 255))
+        assert g[j] != 255
+        return (t * T + j) * wb + int(g[j])
+
+    def oracle_tile(self, t):
+        """The oracle's bit-serial decode of tile t of the library's stream."""
+        lens, _ = ed.codebook_arrays(self.cb)
+        p0, p1 = int(self.hs.block_out_pos[t]), int(self.hs.block_out_pos[t + 1])
+        if p1 == p0:
+            return p0, np.zeros(0, np.uint16)
+        return p0, oracle.decode(self.hs.stream, self.tile_start_bit(t), self.hs.total_bits, lens,
+                                 self.hs.sm[p0:p1], p1 - p0)
+
+
+def check_identity(u, label, poisons=(-1, 0)):
+    ref = _dev_i16(_cat(u.tensors))
+    for p in poisons:
+        out, st = u.decompress(p, label)
+        assert st == 0
+        assert torch.equal(out, ref), f"{label}: mismatches={int((out != ref).sum())}"
+    return out
+
+
+def check_sampled_tiles(u, out, n_samples=24, seed=0):
+    rng = np.random.default_rng(seed)
+    nt = int(u.hs.n_tiles)
+    tiles = sorted(set([0, nt - 1, nt // 2, *rng.integers(0, nt, size=n_samples).tolist()]))
+    host = out.cpu().numpy().view(np.uint16)
+    for t in tiles:
+        p0, dec = u.oracle_tile(t)
+        assert np.array_equal(host[p0:p0 + dec.size], dec), t
+
+
+# ------------------------------------------------------------------ small, exhaustive
+
+
+@pytest.mark.parametrize("bpt", [8, 16])
+def test_config0_every_output_equals_the_oracle(bpt, unit_tensors):
+    (w,) = unit_tensors("0")
+    ocb = oracle.codebook(w)
+    enc = oracle.encode(w, ocb)
+    odec = oracle.decode(enc.stream, 0, enc.total_bits, ocb.lens, enc.sm)
+    u = Unit([w], bpt)
+    assert u.hs.n_tiles > 1 and u.hs.total_bits % (8 * T * bpt) != 0  # ragged last tile
+    out, st = u.decompress(-1, f"cfg0 B={bpt}")
+    assert st == 0
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, odec)
+    assert np.array_equal(got, w)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_multi_tensor_units(seed):
+    rng = np.random.default_rng(1000 + seed)
+    ntens = int(rng.integers(1, 6))
+    tensors = []
+    for _ in range(ntens):
+        n = int(rng.integers(0, 200_000)) // 8 * 8 if seed % 2 else int(rng.integers(0, 200_000))
+        sigma = float(rng.choice([0.02, 0.002, 1.0]))
+        z = (rng.standard_normal(n).astype(np.float32) * sigma).view(np.uint32) >> 16
+        tensors.append(z.astype(np.uint16))
+    if sum(t.size for t in tensors) == 0:
+        tensors.append(np.array([0x3F80], dtype=np.uint16))
+    bpt = 8 if seed % 3 else 16
+    u = Unit(tensors, bpt)
+    out = check_identity(u, f"random seed={seed}")
+    check_sampled_tiles(u, out, 8, seed)
+    offs = u.hs.tensor_offsets
+    for k in range(len(tensors)):
+        if offs[k] % 8:
+            with pytest.raises(ed.Df11Error) as e:
+                ed.df11_decompress_tensor(u.ds, k, torch.empty(max(1, tensors[k].size),
+                                                              dtype=torch.int16, device="cuda"))
+            assert e.value.status == ed.DF11_E_INVALID
+            continue
+        got, st = u.decompress_tensor(k, -1, f"random seed={seed}")
+        assert st == 0 and torch.equal(got, _dev_i16(tensors[k]))
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 8, 9, 2047, 2048 * 8 + 3])
+def test_tiny_and_ragged_sizes(n):
+    rng = np.random.default_rng(n)
+    w = ((rng.standard_normal(n).astype(np.float32) * 0.02).view(np.uint32) >> 16).astype(np.uint16)
+    check_identity(Unit([w]), f"n={n}")
+
+
+def test_single_exponent_one_bit_codes():
+    # every code is 1 bit: 64 symbols per window, the staging buffer's worst case
+    w = (np.arange(300_000, dtype=np.uint32) * 2654435761 % 65536).astype(np.uint16)
+    w = (w & np.uint16(0x807F)) | np.uint16(121 << 7)
+    u = Unit([w])
+    assert u.hs.max_tile_symbols == 8 * 8 * T
+    check_identity(u, "single exponent")
+
+
+def test_every_bit_pattern_including_nan_inf_subnormal():
+    w = np.tile(np.arange(1 << 16, dtype=np.uint16), 3)
+    np.random.default_rng(7).shuffle(w)
+    check_identity(Unit([w]), "all bit patterns")
+
+
+def test_special_values():
+    specials = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81, 0x0001, 0x807F,
+                         0x0080, 0x3F80, 0xBF80], dtype=np.uint16)
+    rng = np.random.default_rng(8)
+    w = ((rng.standard_normal(100_000).astype(np.float32) * 0.02).view(np.uint32) >> 16)
+    w = w.astype(np.uint16)
+    w[rng.integers(0, w.size, 5000)] = rng.choice(specials, 5000)
+    check_identity(Unit([w]), "specials")
+
+
+def test_32_bit_codes_walk_four_table_levels():
+    f = [1, 1]
+    while len(f) < 36:
+        f.append(f[-1] + f[-2])
+    sym = np.repeat(np.arange(36, dtype=np.uint16) + 90, f)
+    np.random.default_rng(9).shuffle(sym)
+    w = ((sym << 7) | (np.arange(sym.size) & 0x807F)).astype(np.uint16)
+    u = Unit([w])
+    assert u.cb.max_len == 32
+    out = check_identity(u, "fibonacci 32-bit codes")
+    check_sampled_tiles(u, out, 8)
+
+
+# ------------------------------------------------------------------ failure paths
+
+
+def test_corrupt_block_out_pos_is_reported_and_tiles_left_unwritten(unit_tensors):
+    (w,) = unit_tensors("0")
+    u = Unit([w])
+    bop = u.hs.block_out_pos.copy()
+    bad = bop.copy()
+    bad[5] += 1  # tiles 4 and 5 now disagree with their decoded counts
+    u.ds.block_out_pos.copy_(torch.from_numpy(bad.view(np.uint8)))
+    out, st = u.decompress(-1, "corrupt bop")
+    assert st == ed.DF11_E_CORRUPT
+    got = out.cpu().numpy().view(np.uint16)
+    # tiles 4, 5 wrote nothing; every other tile is exact
+    lo, hi = int(bad[4]), int(bad[6])
+    assert (got[lo + 8:hi - 8] == 0xFFFF).all()
+    assert np.array_equal(got[: int(bop[4])], w[: int(bop[4])])
+    assert np.array_equal(got[int(bop[6]):], w[int(bop[6]):])
+
+
+def test_corrupt_gap_is_reported(unit_tensors):
+    (w,) = unit_tensors("0")
+    u = Unit([w])
+    gaps = u.hs.gaps.copy()
+    gaps[3 * T + 17] = 255  # a window whose codes are now skipped
+    u.ds.gaps.copy_(torch.from_numpy(gaps))
+    _, st = u.decompress(-1, "corrupt gap")
+    assert st == ed.DF11_E_CORRUPT
+
+
+def test_invalid_arguments_are_rejected_before_launch(unit_tensors):
+    (w,) = unit_tensors("0")
+    u = Unit([w])
+    buf = torch.empty(u.n + 8, dtype=torch.int16, device="cuda")
+    with pytest.raises(ed.Df11Error) as e:
+        ed.df11_decompress_block(u.ds, buf[1:])  # 2-byte aligned only
+    assert e.value.status == ed.DF11_E_INVALID
+    d = u.ds.desc
+    saved = d.n_tiles
+    d.n_tiles = saved + 1
+    with pytest.raises(ed.Df11Error):
+        ed.df11_decompress_block(u.ds, buf)
+    d.n_tiles = saved
+    with pytest.raises(ed.Df11Error):
+        ed.df11_decompress_tensor(u.ds, 1, buf)
+
+
+def test_empty_unit_launches_nothing():
+    d = ed.df11_device_stream()
+    d.threads, d.bytes_per_thread = 256, 8
+    rc = ed.LIB.df11_decompress_block(ed.ctypes.byref(d), None, None, None)
+    assert rc == ed.DF11_OK
+
+
+def test_launch_on_a_side_stream(unit_tensors):
+    (w,) = unit_tensors("0")
+    u = Unit([w])
+    s = torch.cuda.Stream()
+    out = torch.zeros(u.n, dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    say("[gpu] df11_decompress_block on a side stream")
+    with torch.cuda.stream(s):
+        ed.df11_decompress_block(u.ds, out, stream=s)
+    s.synchronize()
+    assert torch.equal(out, _dev_i16(w))
+
+
+# ------------------------------------------------------------------ full workloads
+
+
+@pytest.mark.parametrize("cfg", ["3a", "3b", "3c"])
+def test_stress_config_full_size(cfg, unit_tensors):
+    u = Unit(unit_tensors(cfg))
+    out = check_identity(u, f"cfg{cfg}", poisons=(-1,))
+    check_sampled_tiles(u, out)
+
+
+@pytest.mark.parametrize("cfg", ["1", "2"])
+def test_block_config_full_size(cfg):
+    unit = sw.config(cfg).units[0]
+    tensors = sw.gen_unit(unit)
+    u = Unit(tensors)
+    out = check_identity(u, f"cfg{cfg} block", poisons=(-1,))
+    check_sampled_tiles(u, out, 16)
+    del out
+    for k in (0, 6):
+        got, st = u.decompress_tensor(k, 0, f"cfg{cfg}")
+        assert st == 0 and torch.equal(got, _dev_i16(tensors[k]))
+
+
+@pytest.mark.parametrize("group", range(6))
+def test_full_model_units(group):
+    """Config 4 (embedding, 32 blocks, lm_head), six units per test case."""
+    cfg = sw.config("4")
+    units = cfg.units[group * 6:(group + 1) * 6]
+    for unit in units:
+        tensors = sw.gen_unit(unit)
+        u = Unit(tensors)
+        check_identity(u, f"cfg4 {unit.name}", poisons=(-1,))
+        del u

@@ -1,0 +1,179 @@
+"""Host half of the library (codebook + encoder) against the oracle, on CPU.
+
+The library and the oracle follow the same tie-break and canonical rules, so
+code lengths, codes, stream bytes, sm bytes, gaps and block_out_pos must be
+equal byte for byte; where package-merge limits lengths, several optimal
+codes exist and only the total size is unique.
+"""
+
+import numpy as np
+import pytest
+
+import entropy_decoding_amd as ed
+import oracle
+
+
+def _compare(tensors, threads=256, bpt=8, expect_same_lengths=True):
+    cb = ed.df11_build_codebook(tensors)
+    lens, codes = ed.codebook_arrays(cb)
+    ocb = oracle.codebook(tensors)
+    assert oracle.kraft_numerator(lens) == 1 << 32
+    assert oracle.total_code_bits(ocb.counts, lens) == oracle.total_code_bits(ocb.counts, ocb.lens)
+    if expect_same_lengths:
+        assert np.array_equal(lens, ocb.lens)
+        assert np.array_equal(codes, ocb.codes)
+    else:
+        ocb = oracle.Codebook(ocb.counts, lens, oracle.canonical_codes(lens))
+        assert np.array_equal(codes, ocb.codes)
+    hs = ed.df11_encode(cb, tensors, threads, bpt)
+    enc = oracle.encode(tensors, ocb)
+    nb = (enc.total_bits + 7) // 8
+    assert hs.total_bits == enc.total_bits
+    assert np.array_equal(hs.stream[:nb], enc.stream)
+    assert not hs.stream[nb:].any()
+    assert hs.stream.size == hs.n_tiles * threads * bpt + ed.DF11_STREAM_PAD
+    n = sum(np.asarray(t).size for t in tensors)
+    assert np.array_equal(hs.sm[:n], enc.sm)
+    assert not hs.sm[n:].any()
+    gaps, bop = oracle.aux(tensors, ocb, threads, bpt)
+    assert np.array_equal(hs.gaps, gaps)
+    assert np.array_equal(hs.block_out_pos, bop)
+    assert hs.max_tile_symbols == (int(np.diff(bop.astype(np.int64)).max()) if bop.size > 1 else 0)
+    # tensor offsets and tile ranges from the oracle's per-tensor start bits
+    assert hs.tensor_offsets.tolist() == [0, *np.cumsum(enc.numel).tolist()]
+    tile_bits = 8 * bpt * threads
+    for k, t in enumerate(tensors):
+        t = np.asarray(t).reshape(-1)
+        if t.size == 0:
+            assert hs.tensor_tiles[2 * k] == hs.tensor_tiles[2 * k + 1]
+            continue
+        first = enc.tensor_start_bits[k] // tile_bits
+        last_len = int(lens[(int(t[-1]) >> 7) & 0xFF])
+        last = (enc.tensor_start_bits[k + 1] - last_len) // tile_bits + 1
+        assert (hs.tensor_tiles[2 * k], hs.tensor_tiles[2 * k + 1]) == (first, last)
+    return cb, hs, ocb, enc
+
+
+def test_config0_matches_oracle(unit_tensors):
+    _compare(unit_tensors("0"))
+
+
+@pytest.mark.parametrize("cfg", ["3a", "3b", "3c"])
+def test_stress_configs_match_oracle(unit_tensors, cfg):
+    (w,) = unit_tensors(cfg)
+    _compare([w[: 1 << 22]])
+
+
+def test_b16_layout_matches_oracle(unit_tensors):
+    _compare(unit_tensors("0"), bpt=16)
+
+
+def test_multi_tensor_unit_with_ragged_and_empty_tensors():
+    rng = np.random.default_rng(11)
+    ts = []
+    for n in (4097, 0, 1, 333_333, 8, 5_000_001 % 700_000):
+        z = (rng.standard_normal(n).astype(np.float32) * 0.02).view(np.uint32) >> 16
+        ts.append(z.astype(np.uint16))
+    _compare(ts)
+
+
+def test_pieces_larger_than_one_encoder_work_item():
+    # > 4 Mi weights per tensor exercises the parallel pieces and their stitching
+    rng = np.random.default_rng(12)
+    z = (rng.standard_normal((1 << 22) + 12345).astype(np.float32) * 0.05).view(np.uint32) >> 16
+    _compare([z.astype(np.uint16), z[:777].astype(np.uint16)])
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 2047, 2048, 2049])
+def test_tiny_units(n):
+    rng = np.random.default_rng(n)
+    w = rng.integers(0, 1 << 16, size=n, dtype=np.uint16)
+    w[::3] = 0x3F80
+    _compare([w])
+
+
+def test_single_exponent_unit():
+    w = (np.arange(50_000, dtype=np.uint16) & np.uint16(0x807F)) | np.uint16(121 << 7)
+    cb, hs, ocb, _ = _compare([w])
+    lens, _ = ed.codebook_arrays(cb)
+    assert lens[121] == 1 and lens[0] == 1 and cb.n_luts == 1
+    assert hs.total_bits == w.size
+
+
+def test_every_bf16_bit_pattern():
+    w = np.arange(1 << 16, dtype=np.uint16)
+    np.random.default_rng(13).shuffle(w)
+    cb, hs, _, _ = _compare([w])
+    assert cb.max_len == 8 and cb.n_luts == 1
+
+
+def _fib_unit(nsym=36):
+    f = [1, 1]
+    while len(f) < nsym:
+        f.append(f[-1] + f[-2])
+    sym = np.repeat(np.arange(nsym, dtype=np.uint16) + 90, f)
+    np.random.default_rng(14).shuffle(sym)
+    return ((sym << 7) | (np.arange(sym.size) & 0x807F)).astype(np.uint16)
+
+
+def test_length_limited_codebook_forced_by_fibonacci_counts():
+    w = _fib_unit()
+    cb, hs, _, _ = _compare([w], expect_same_lengths=False)
+    assert cb.max_len == 32
+    assert cb.n_luts >= 4
+
+
+def test_lut_entries_resolve_every_code():
+    """Walk the library's tables for every code, as a decoder would."""
+    w = _fib_unit()
+    cb = ed.df11_build_codebook([w])
+    lens, codes = ed.codebook_arrays(cb)
+    lut = np.ctypeslib.as_array(cb.lut)
+    for s in np.nonzero(lens)[0]:
+        l = int(lens[s])
+        v = int(codes[s]) << (32 - l)
+        table, lvl = 0, 0
+        while True:
+            e = int(lut[table][(v >> (24 - 8 * lvl)) & 0xFF])
+            if e & 0x8000:
+                table, lvl = e & 0x7FFF, lvl + 1
+                assert table < cb.n_luts and lvl < 4
+                continue
+            assert (e >> 8) & 0x3F == l and e & 0xFF == s
+            break
+
+
+def test_errors():
+    w = np.zeros(10, dtype=np.uint16) | np.uint16(100 << 7)
+    cb = ed.df11_build_codebook([w])
+    other = np.full(4, 50 << 7, dtype=np.uint16)
+    with pytest.raises(ed.Df11Error) as e:
+        ed.df11_encode(cb, [other])
+    assert e.value.status == ed.DF11_E_SYMBOL
+    with pytest.raises(ed.Df11Error) as e:
+        ed.df11_encode(cb, [w], threads=128)
+    assert e.value.status == ed.DF11_E_INVALID
+    with pytest.raises(ed.Df11Error) as e:
+        ed.df11_build_codebook([np.zeros(0, dtype=np.uint16)])
+    assert e.value.status == ed.DF11_E_INVALID
+
+
+def test_lut_budget_error():
+    # dyadic counts force the lengths: 64 symbols of 7 bits, 64 of 8, 128 of 9.
+    # The 9-bit codes fill 64 distinct 8-bit prefixes, so the root needs 64
+    # second-level tables: 65 in all, one over the budget.
+    counts = np.zeros(256, dtype=np.int64)
+    counts[:64], counts[64:128], counts[128:] = 4, 2, 1
+    w = np.repeat(np.arange(256, dtype=np.uint16) << 7, counts)
+    ocb = oracle.codebook(w)
+    assert sorted(set(ocb.lens.tolist())) == [7, 8, 9]
+    with pytest.raises(ed.Df11Error) as e:
+        ed.df11_build_codebook([w])
+    assert e.value.status == ed.DF11_E_LUT_BUDGET
+    # one 9-bit prefix fewer fits: merge two 9-bit pairs into 8-bit codes
+    counts[128:] = 1
+    counts[126:128] = 0
+    counts[128:130] = 2
+    w = np.repeat(np.arange(256, dtype=np.uint16) << 7, counts)
+    cb = ed.df11_build_codebook([w])
+    assert cb.n_luts <= ed.DF11_MAX_LUTS
