@@ -169,6 +169,9 @@ def main():
     ap.add_argument("--config", default="2")
     ap.add_argument("--bpt", type=int, default=8, choices=(8, 16))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="time a plain device-to-device copy of this many bytes instead "
+                         "(the achievable-bandwidth reference and the counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decoder needs no cross-GPU exchange and this "
@@ -182,6 +185,8 @@ def main():
     import synth_weights as sw
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    if args.copy_bytes:
+        return copy_reference(args, torch)
     cfg = sw.config(args.config)
     if len(cfg.units) != 1:
         return stream_units(cfg, args, torch, ed, sw)
@@ -239,6 +244,30 @@ def main():
     print(json.dumps(line), flush=True)
     if not r["exact"]:
         sys.exit(1)
+
+
+def copy_reference(args, torch):
+    """A plain copy: reads and writes copy_bytes each launch."""
+    n = args.copy_bytes // 4
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    moved = 2 * 4 * n
+    print(json.dumps({"metric": "device copy GB/s (read + write)",
+                      "value": round(moved / (ms.mean() * 1e-3) / 1e9, 1), "unit": "GB/s",
+                      "bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
+                      "ms_mean": round(float(ms.mean()), 4), "steps": args.steps}), flush=True)
 
 
 def stream_units(cfg, args, torch, ed, sw):
