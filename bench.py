@@ -45,8 +45,10 @@ def kernel_hash() -> str:
 def algorithmic_bytes(hs, cb) -> int:
     """Compressed arrays read once (stream payload, sm, gaps, block_out_pos, tables)
     plus 2 bytes of BF16 written per weight."""
+    import entropy_decoding_amd as ed
+
     read = (hs.total_bits + 7) // 8 + hs.n_weights + hs.gaps.size + 4 * hs.block_out_pos.size \
-        + 512 * cb.n_luts
+        + ed.table_bytes(cb)
     return int(read + 2 * hs.n_weights)
 
 

@@ -25,6 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libdf11.so")
 DF11_MAX_CODE_LEN = 32
 DF11_MAX_LUTS = 64
 DF11_STREAM_PAD = 16
+DF11_MULTI_BITS = 10
+DF11_COUNT_BITS = 12
 
 DF11_OK = 0
 DF11_E_INVALID = 1
@@ -56,6 +58,8 @@ class df11_codebook(ctypes.Structure):
         ("code", ctypes.c_uint32 * 256),
         ("n_luts", ctypes.c_uint32),
         ("max_len", ctypes.c_uint32),
+        ("multi", ctypes.c_uint32 * (1 << DF11_MULTI_BITS)),
+        ("count", ctypes.c_uint16 * (1 << DF11_COUNT_BITS)),
         ("lut", (ctypes.c_uint16 * 256) * DF11_MAX_LUTS),
     ]
 
@@ -94,7 +98,7 @@ class df11_device_stream(ctypes.Structure):
         ("sm", ctypes.c_void_p),
         ("gaps", ctypes.c_void_p),
         ("block_out_pos", ctypes.c_void_p),
-        ("lut", ctypes.c_void_p),
+        ("tables", ctypes.c_void_p),
         ("tensor_offsets", _u64p),
         ("tensor_tiles", _u64p),
         ("n_weights", ctypes.c_uint64),
@@ -213,7 +217,7 @@ class HostStream:
             "block_out_pos": 4 * self.block_out_pos.size,
         }
         if cb is not None:
-            d["lut"] = 512 * cb.n_luts
+            d["tables"] = table_bytes(cb)
         return d
 
 
@@ -268,8 +272,7 @@ class DeviceStream:
         self.sm = up(hs.sm)
         self.gaps = up(hs.gaps if hs.gaps.size else np.zeros(1, np.uint8))
         self.block_out_pos = up(hs.block_out_pos)
-        lut = np.ctypeslib.as_array(cb.lut).reshape(-1)[: 256 * cb.n_luts].copy()
-        self.lut = up(lut)
+        self.tables = up(table_image(cb))
         self.tensor_offsets = np.ascontiguousarray(hs.tensor_offsets, dtype=np.uint64)
         self.tensor_tiles = np.ascontiguousarray(
             hs.tensor_tiles if hs.tensor_tiles.size else np.zeros(2, np.uint64), dtype=np.uint64)
@@ -278,7 +281,7 @@ class DeviceStream:
         d.sm = self.sm.data_ptr()
         d.gaps = self.gaps.data_ptr()
         d.block_out_pos = self.block_out_pos.data_ptr()
-        d.lut = self.lut.data_ptr()
+        d.tables = self.tables.data_ptr()
         d.tensor_offsets = self.tensor_offsets.ctypes.data_as(_u64p)
         d.tensor_tiles = self.tensor_tiles.ctypes.data_as(_u64p)
         d.n_weights = hs.n_weights
@@ -297,7 +300,7 @@ class DeviceStream:
 
     def device_bytes(self) -> int:
         return sum(t.numel() for t in (self.stream, self.sm, self.gaps, self.block_out_pos,
-                                       self.lut))
+                                       self.tables))
 
 
 def _stream_handle(stream):
@@ -331,6 +334,18 @@ def df11_decompress_tensor(ds: DeviceStream, k: int, out, status=None, stream=No
            LIB.df11_decompress_tensor(ctypes.byref(ds.desc), int(k),
                                       ctypes.c_void_p(out.data_ptr()), sp,
                                       _stream_handle(stream)))
+
+
+def table_bytes(cb: df11_codebook) -> int:
+    """df11_table_bytes(): multi-symbol, count and n_luts hierarchical tables."""
+    return ctypes.sizeof(cb.multi) + ctypes.sizeof(cb.count) + 512 * int(cb.n_luts)
+
+
+def table_image(cb: df11_codebook) -> np.ndarray:
+    """The device copy of the codebook's tables (bytes from cb.multi onward)."""
+    start = df11_codebook.multi.offset
+    raw = ctypes.string_at(ctypes.addressof(cb) + start, table_bytes(cb))
+    return np.frombuffer(raw, dtype=np.uint8).copy()
 
 
 def codebook_arrays(cb: df11_codebook):

@@ -236,6 +236,49 @@ int build_luts(df11_codebook *cb) {
     return DF11_OK;
 }
 
+// Length and symbol of the code at the head of a 32-bit left-aligned value,
+// by walking the hierarchical tables; length 0 if no leaf is reached.
+void head_code(const df11_codebook *cb, uint32_t v, uint32_t &len, uint32_t &sym) {
+    uint32_t e = cb->lut[0][v >> 24];
+    for (int lvl = 1; (e & 0x8000) && lvl < 4; lvl++)
+        e = cb->lut[e & 0x7FFF][(v >> (24 - 8 * lvl)) & 0xFF];
+    len = (e & 0x8000) ? 0 : (e >> 8) & 0x3F;
+    sym = e & 0xFF;
+}
+
+// Multi-code tables for the decoder's fast path.  Bits beyond the index are
+// taken as zero: a code that fits in the remaining index bits is decoded the
+// same whatever follows, and one that does not fit comes out longer than
+// the remaining bits, so it is left out.
+void build_multi_tables(df11_codebook *cb) {
+    constexpr uint32_t kM = DF11_MULTI_BITS, kC = DF11_COUNT_BITS;
+    for (uint32_t x = 0; x < (1u << kM); x++) {
+        const uint32_t v = x << (32 - kM);
+        uint32_t used = 0, n = 0, syms = 0;
+        while (n < 3) {
+            uint32_t len, sym;
+            head_code(cb, v << used, len, sym);
+            if (len == 0 || used + len > kM) break;
+            syms |= sym << (8 * n);
+            n++;
+            used += len;
+        }
+        cb->multi[x] = n ? (n << 30) | (used << 24) | syms : 0;
+    }
+    for (uint32_t x = 0; x < (1u << kC); x++) {
+        const uint32_t v = x << (32 - kC);
+        uint32_t used = 0, mask = 0;
+        for (;;) {
+            uint32_t len, sym;
+            head_code(cb, v << used, len, sym);
+            if (len == 0 || used + len > kC) break;
+            mask |= 1u << used;
+            used += len;
+        }
+        cb->count[x] = uint16_t(used ? (used << 12) | mask : 0);
+    }
+}
+
 bool valid_layout(uint32_t T, uint32_t B) { return T == 256 && (B == 8 || B == 16); }
 
 int log2u(uint64_t x) {
@@ -384,7 +427,10 @@ int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel, u
         if (mx > DF11_MAX_CODE_LEN) mx = package_merge(counts, DF11_MAX_CODE_LEN, cb->code_len);
         cb->max_len = uint32_t(mx);
         canonical(cb->code_len, cb->code);
-        return build_luts(cb);
+        int rc = build_luts(cb);
+        if (rc != DF11_OK) return rc;
+        build_multi_tables(cb);
+        return DF11_OK;
     } catch (...) {
         return DF11_E_INVALID;
     }

@@ -63,21 +63,46 @@ typedef enum df11_status {
 /* An opaque hipStream_t (0 = the null stream). */
 typedef void *df11_hip_stream;
 
+#define DF11_MULTI_BITS 10      /* index width of the multi-symbol decode table */
+#define DF11_COUNT_BITS 12      /* index width of the code-start (count) table */
+
 /*
- * Codebook (caller-owned POD, about 34 KiB).  code_len[s] == 0 means symbol s
- * has no code.  lut holds n_luts tables of 256 uint16 entries; table 0 is
- * indexed by the top 8 bits of a 32-bit left-aligned window of the stream,
- * a level-k table by the next 8 bits.  Entry formats:
- *   leaf     bit 15 = 0, bits 13..8 = full code length (1..32), bits 7..0 = symbol
- *   pointer  bit 15 = 1, bits 14..0 = index of the next-level table
+ * Codebook (caller-owned POD, about 46 KiB).  code_len[s] == 0 means symbol s
+ * has no code.  Three kinds of 8-bit-or-wider-indexed tables are derived from
+ * the codes ("compact, hierarchical lookup tables", DFloat11 abstract); each is
+ * indexed by the leading bits of the stream at a code boundary, MSB-first:
+ *
+ *   lut[k][256]  hierarchical single-code tables.  Table 0 is indexed by the
+ *                top 8 bits of a 32-bit left-aligned window, a level-k table
+ *                by the next 8 bits.  Entries:
+ *                  leaf     bit 15 = 0, bits 13..8 = code length (1..32), bits 7..0 = symbol
+ *                  pointer  bit 15 = 1, bits 14..0 = index of the next-level table
+ *   multi[1024]  10-bit index; the first up-to-3 codes that lie wholly inside
+ *                the 10 bits: bits 31..30 = how many (0 when the first code is
+ *                longer than 10 bits), bits 29..24 = their total length, bits
+ *                7..0, 15..8, 23..16 = their symbols in order (unused slots 0).
+ *   count[4096]  12-bit index; every code that lies wholly inside the 12 bits:
+ *                bits 15..12 = their total length (0 when the first code is
+ *                longer than 12 bits), bit j (j < 12) set iff one of them starts
+ *                j bits after the index's first bit.
+ *
+ * multi, count and lut[0 .. n_luts) are contiguous: the device copy of the
+ * tables is the df11_table_bytes(cb) bytes starting at &cb->multi[0].
  */
 typedef struct df11_codebook {
     uint8_t code_len[256];
     uint32_t code[256];
     uint32_t n_luts;
     uint32_t max_len;
+    uint32_t multi[1u << DF11_MULTI_BITS];
+    uint16_t count[1u << DF11_COUNT_BITS];
     uint16_t lut[DF11_MAX_LUTS][256];
 } df11_codebook;
+
+/* Bytes of the device table image of cb (multi, count, then n_luts hierarchical tables). */
+static inline size_t df11_table_bytes(const df11_codebook *cb) {
+    return sizeof(cb->multi) + sizeof(cb->count) + (size_t)cb->n_luts * 256 * sizeof(uint16_t);
+}
 
 /* Exact sizes of everything df11_encode writes, for caller allocation. */
 typedef struct df11_sizes {
@@ -115,7 +140,8 @@ typedef struct df11_host_stream {
 
 /*
  * A compressed unit in DEVICE memory, as df11_decompress_* read it.  Device
- * pointers: stream, sm (16-byte aligned), gaps, block_out_pos, lut.  Host
+ * pointers: stream, sm and tables (16-byte aligned), gaps, block_out_pos;
+ * tables holds the df11_table_bytes(cb) bytes starting at &cb->multi[0].  Host
  * pointers: tensor_offsets and tensor_tiles (read synchronously by
  * df11_decompress_tensor only; may be null for df11_decompress_block).
  * Scalars are copied from the df11_host_stream and df11_codebook they came from.
@@ -125,7 +151,7 @@ typedef struct df11_device_stream {
     const uint8_t *sm;
     const uint8_t *gaps;
     const uint32_t *block_out_pos;
-    const uint16_t *lut;
+    const void *tables;
     const uint64_t *tensor_offsets;
     const uint64_t *tensor_tiles;
     uint64_t n_weights;

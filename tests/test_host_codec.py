@@ -177,3 +177,52 @@ def test_lut_budget_error():
     w = np.repeat(np.arange(256, dtype=np.uint16) << 7, counts)
     cb = ed.df11_build_codebook([w])
     assert cb.n_luts <= ed.DF11_MAX_LUTS
+
+
+def _greedy_codes(bits: str, table):
+    """Codes decoded from the front of a bit string until one does not fit."""
+    out, pos = [], 0
+    while True:
+        for l in range(1, len(bits) - pos + 1):
+            s = table.get((l, bits[pos:pos + l]))
+            if s is not None:
+                out.append((pos, l, s))
+                pos += l
+                break
+        else:
+            return out
+
+
+@pytest.mark.parametrize("which", ["cfg0", "one_exponent", "fibonacci", "uniform"])
+def test_fast_tables_match_a_brute_force_decode(which, unit_tensors):
+    if which == "cfg0":
+        w = unit_tensors("0")[0]
+    elif which == "one_exponent":
+        w = (np.arange(5000, dtype=np.uint16) & np.uint16(0x807F)) | np.uint16(121 << 7)
+        w[::50] = 0x3F80
+    elif which == "fibonacci":
+        w = _fib_unit()
+    else:
+        w = np.arange(1 << 16, dtype=np.uint16)
+    cb = ed.df11_build_codebook([w])
+    ocb = oracle.codebook([w])
+    lens, codes = ed.codebook_arrays(cb)
+    assert np.array_equal(lens, ocb.lens) or which == "fibonacci"
+    table = {(int(l), format(int(codes[s]), f"0{int(l)}b")): s for s, l in enumerate(lens) if l}
+    multi = np.ctypeslib.as_array(cb.multi)
+    count = np.ctypeslib.as_array(cb.count)
+    kM, kC = ed.DF11_MULTI_BITS, ed.DF11_COUNT_BITS
+    for x in range(1 << kM):
+        got = _greedy_codes(format(x, f"0{kM}b"), table)[:3]
+        e = int(multi[x])
+        assert e >> 30 == len(got), x
+        assert (e >> 24) & 0x3F == sum(l for _, l, _ in got), x
+        for i, (_, _, s) in enumerate(got):
+            assert (e >> (8 * i)) & 0xFF == s, x
+        for i in range(len(got), 3):
+            assert (e >> (8 * i)) & 0xFF == 0
+    for x in range(1 << kC):
+        got = _greedy_codes(format(x, f"0{kC}b"), table)
+        e = int(count[x])
+        assert e >> 12 == sum(l for _, l, _ in got), x
+        assert e & 0xFFF == sum(1 << pos for pos, _, _ in got), x
