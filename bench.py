@@ -9,7 +9,7 @@ written, whole job over K steps), plus the dominant kernel's HBM roofline
 fraction from algorithmic bytes (compressed arrays read once + BF16 written)
 and the CPU oracle's bit-serial decode timed on this host as a baseline.
 
-  python bench.py [--steps K] [--warmup W] [--config 2|1|0|3a|3b|3c|4] [--bpt 8|16]
+  python bench.py [--steps K] [--warmup W] [--config 2|1|0|3a|3b|3c|4] [--tile-windows 256|512]
 """
 
 from __future__ import annotations
@@ -52,14 +52,14 @@ def algorithmic_bytes(hs, cb) -> int:
     return int(read + 2 * hs.n_weights)
 
 
-def measured_traffic(workload: str, bpt: int):
+def measured_traffic(workload: str, tile_windows: int):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    r = rec.get(f"{workload}/B{bpt}")
+    r = rec.get(f"{workload}/T{tile_windows}")
     if not r or r.get("kernel_sha") != kernel_hash():
         return None
     return r.get("bytes_per_launch")
@@ -119,7 +119,7 @@ def run_unit(name, tensors, args, torch, ed):
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     cb = ed.df11_build_codebook(tensors)
-    hs = ed.df11_encode(cb, tensors, 256, args.bpt)
+    hs = ed.df11_encode(cb, tensors, args.tile_windows, 8)
     log(f"[bench] {name}: encoded {hs.n_weights} weights in {time.perf_counter() - t0:.1f} s, "
         f"{hs.n_tiles} tiles, luts={cb.n_luts}, max_len={cb.max_len}")
     ds = ed.DeviceStream(hs, cb, dev)
@@ -169,7 +169,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="2")
-    ap.add_argument("--bpt", type=int, default=8, choices=(8, 16))
+    ap.add_argument("--tile-windows", type=int, default=256, choices=(256, 512))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes instead "
@@ -205,7 +205,7 @@ def main():
         value = 2 * n * args.steps / (kms.sum() * 1e-3) / 1e9  # flush kernels excluded
     else:
         value = 2 * n * args.steps / r["wall_s"] / 1e9
-    traffic = measured_traffic(cfg.name, args.bpt)
+    traffic = measured_traffic(cfg.name, args.tile_windows)
     line = {
         "metric": "decompressed BF16 GB/s",
         "value": round(value, 2),
@@ -222,7 +222,7 @@ def main():
         "config": {
             "workload": cfg.name,
             "n_weights": n,
-            "layout": f"T256xB{args.bpt}",
+            "layout": f"T{args.tile_windows}xB8",
             "bit_exact": bool(r["exact"]),
             "bits_per_weight_payload": round(r["payload_bpw"], 4),
             "bits_per_weight_total": round(r["total_bpw"], 4),
@@ -281,7 +281,7 @@ def stream_units(cfg, args, torch, ed, sw):
     for unit in cfg.units:
         tensors = sw.gen_unit(unit)
         cb = ed.df11_build_codebook(tensors)
-        hs = ed.df11_encode(cb, tensors, 256, args.bpt)
+        hs = ed.df11_encode(cb, tensors, args.tile_windows, 8)
         ds = ed.DeviceStream(hs, cb, dev)
         ref_hash = None
         units.append((unit, ds, hs, cb, tensors if cfg.index != 4 else None))
@@ -330,7 +330,7 @@ def stream_units(cfg, args, torch, ed, sw):
         "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
         "config": {
             "workload": cfg.name, "n_weights": n_total, "units": len(units),
-            "layout": f"T256xB{args.bpt}", "bit_exact": bool(exact),
+            "layout": f"T{args.tile_windows}xB8", "bit_exact": bool(exact),
             "unit_ms_p50": round(float(np.percentile(lat, 50)), 4),
             "unit_ms_p99": round(float(np.percentile(lat, 99)), 4),
             "block_ms_p50": round(float(np.percentile(blocks, 50)), 4) if blocks.size else None,

@@ -36,8 +36,8 @@ DF11_E_CAPACITY = 4
 DF11_E_HIP = 5
 DF11_E_CORRUPT = 6
 
-DEFAULT_THREADS = 256
-DEFAULT_BYTES_PER_THREAD = 8
+DEFAULT_TILE_WINDOWS = 256
+DEFAULT_WINDOW_BYTES = 8
 
 
 class Df11Error(RuntimeError):
@@ -83,8 +83,8 @@ class df11_host_stream(ctypes.Structure):
         ("gaps_capacity", ctypes.c_uint64),
         ("bop_capacity", ctypes.c_uint64),
         ("n_tensors", ctypes.c_uint32),
-        ("threads", ctypes.c_uint32),
-        ("bytes_per_thread", ctypes.c_uint32),
+        ("tile_windows", ctypes.c_uint32),
+        ("window_bytes", ctypes.c_uint32),
         ("max_tile_symbols", ctypes.c_uint32),
         ("n_weights", ctypes.c_uint64),
         ("total_bits", ctypes.c_uint64),
@@ -105,8 +105,8 @@ class df11_device_stream(ctypes.Structure):
         ("total_bits", ctypes.c_uint64),
         ("n_tiles", ctypes.c_uint64),
         ("n_luts", ctypes.c_uint32),
-        ("threads", ctypes.c_uint32),
-        ("bytes_per_thread", ctypes.c_uint32),
+        ("tile_windows", ctypes.c_uint32),
+        ("window_bytes", ctypes.c_uint32),
         ("max_tile_symbols", ctypes.c_uint32),
         ("n_tensors", ctypes.c_uint32),
     ]
@@ -178,12 +178,12 @@ def df11_build_codebook(tensors) -> df11_codebook:
     return cb
 
 
-def df11_encode_size(cb: df11_codebook, tensors, threads: int = DEFAULT_THREADS,
-                     bytes_per_thread: int = DEFAULT_BYTES_PER_THREAD) -> df11_sizes:
+def df11_encode_size(cb: df11_codebook, tensors, tile_windows: int = DEFAULT_TILE_WINDOWS,
+                     window_bytes: int = DEFAULT_WINDOW_BYTES) -> df11_sizes:
     arrs, ptrs, numel, n = _tensor_args(tensors)
     sz = df11_sizes()
-    _check("df11_encode_size", LIB.df11_encode_size(ctypes.byref(cb), ptrs, numel, n, threads,
-                                                    bytes_per_thread, ctypes.byref(sz)))
+    _check("df11_encode_size", LIB.df11_encode_size(ctypes.byref(cb), ptrs, numel, n, tile_windows,
+                                                    window_bytes, ctypes.byref(sz)))
     return sz
 
 
@@ -197,8 +197,8 @@ class HostStream:
     block_out_pos: np.ndarray
     tensor_offsets: np.ndarray
     tensor_tiles: np.ndarray
-    threads: int
-    bytes_per_thread: int
+    tile_windows: int
+    window_bytes: int
     max_tile_symbols: int
     n_weights: int
     total_bits: int
@@ -221,10 +221,10 @@ class HostStream:
         return d
 
 
-def df11_encode(cb: df11_codebook, tensors, threads: int = DEFAULT_THREADS,
-                bytes_per_thread: int = DEFAULT_BYTES_PER_THREAD) -> HostStream:
+def df11_encode(cb: df11_codebook, tensors, tile_windows: int = DEFAULT_TILE_WINDOWS,
+                window_bytes: int = DEFAULT_WINDOW_BYTES) -> HostStream:
     arrs, ptrs, numel, n = _tensor_args(tensors)
-    sz = df11_encode_size(cb, arrs, threads, bytes_per_thread)
+    sz = df11_encode_size(cb, arrs, tile_windows, window_bytes)
     stream = np.empty(sz.stream_bytes, dtype=np.uint8)
     sm = np.empty(sz.sm_bytes, dtype=np.uint8)
     gaps = np.empty(max(1, sz.n_windows), dtype=np.uint8)
@@ -243,10 +243,10 @@ def df11_encode(cb: df11_codebook, tensors, threads: int = DEFAULT_THREADS,
     hs.gaps_capacity = sz.n_windows
     hs.bop_capacity = bop.size
     hs.n_tensors = n
-    _check("df11_encode", LIB.df11_encode(ctypes.byref(cb), ptrs, numel, n, threads,
-                                          bytes_per_thread, ctypes.byref(hs)))
+    _check("df11_encode", LIB.df11_encode(ctypes.byref(cb), ptrs, numel, n, tile_windows,
+                                          window_bytes, ctypes.byref(hs)))
     return HostStream(stream, sm, gaps[: sz.n_windows], bop, offs, tiles[: 2 * n],
-                      hs.threads, hs.bytes_per_thread, hs.max_tile_symbols, hs.n_weights,
+                      hs.tile_windows, hs.window_bytes, hs.max_tile_symbols, hs.n_weights,
                       hs.total_bits, hs.n_tiles)
 
 
@@ -288,8 +288,8 @@ class DeviceStream:
         d.total_bits = hs.total_bits
         d.n_tiles = hs.n_tiles
         d.n_luts = cb.n_luts
-        d.threads = hs.threads
-        d.bytes_per_thread = hs.bytes_per_thread
+        d.tile_windows = hs.tile_windows
+        d.window_bytes = hs.window_bytes
         d.max_tile_symbols = hs.max_tile_symbols
         d.n_tensors = hs.n_tensors
         self.desc = d

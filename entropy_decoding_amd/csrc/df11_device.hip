@@ -8,28 +8,35 @@
 // kernel's organisation is this library's own, for CDNA4:
 //
 // * A persistent grid (as many workgroups as fit on the device at once) walks
-//   the tiles; each workgroup copies the tables into LDS once.
-// * Per tile of T*B stream bytes, thread t owns window t:
-//     - one vector load of its B bytes plus the 4 bytes after them, its gap
-//       byte, and (issued early, consumed last) the sign+mantissa bytes of
-//       the tile's outputs;
-//     - phase 1 counts the codes that start in the window, several per step:
-//       a 12-bit index into the count table gives the start offsets of every
-//       code wholly inside those 12 bits as a bit mask, so a step adds the
-//       popcount of the mask cut at the window's end;
-//     - a wave64 inclusive scan in DPP row shifts and row broadcasts, then an
-//       LDS pass over the T/64 wave totals, turns counts into offsets; the
-//       tile total must equal block_out_pos[t+1] - block_out_pos[t];
-//     - phase 2 walks the window again with a 10-bit index into the
-//       multi-symbol table (up to 3 exponents per step) and writes exponent
-//       bytes into an LDS staging buffer at their offsets; a step writes all 3
-//       slots, so the last step may spill up to 2 bytes onto the next
-//       thread's first two outputs, which every thread rewrites after a
-//       barrier;
-//     - the outputs are assembled 16 at a time from 16 sm bytes and 16
-//       exponent bytes with byte permutes and written with 16-byte stores.
-//   Codes longer than the fast tables' index walk the hierarchical 8-bit
-//   tables (up to 4 levels for 32-bit codes).
+//   the tiles; each workgroup copies the tables into LDS once.  A tile is
+//   256*C windows of 8 bytes; thread t decodes windows C*t .. C*t + C - 1 as
+//   C independent dependency chains, so each LDS lookup latency is shared by C
+//   codes in flight.
+// * The next tile's window bytes, gaps and bounds are loaded before the
+//   current tile's stores are issued: CDNA counts loads and stores with one
+//   in-order counter, so waiting for a load issued after a store would wait
+//   for the store.  Bounds arrive through a vector load: a scalar load would
+//   share its counter with LDS and stall the decode loops.
+// * Phase 1 counts the codes that start in each window, several per step: a
+//   12-bit index into the count table gives the start offsets of every code
+//   wholly inside those 12 bits as a bit mask, so a step adds the popcount of
+//   the mask cut at the window's end.
+// * A wave64 inclusive scan in DPP row shifts and row broadcasts, then an LDS
+//   pass over the 4 wave totals, turns counts into offsets; the tile total
+//   must equal block_out_pos[t+1] - block_out_pos[t].
+// * Phase 2 walks the windows again with a 10-bit index into the
+//   multi-symbol table (up to 3 exponents per step) and writes exponent bytes
+//   into an LDS staging buffer at their offsets.  A step writes all 3 slots,
+//   so a window's last step may spill up to 2 bytes onto the next window's
+//   first two outputs; every window rewrites those after a barrier.
+// * The decode loops are wave-uniform: they run until no lane has work
+//   (ballot), finished chains are masked by selects and their writes go to
+//   the lane's own trash slot (stores from many lanes to one address would be
+//   serialised), so no exec-mask bookkeeping sits in the dependency chain.
+// * The outputs are assembled 8 at a time from 8 sm bytes and 8 exponent
+//   bytes with byte permutes; the lanes of a wave store 1 KiB contiguously.
+// Codes longer than the fast tables' index walk the hierarchical 8-bit
+// tables (up to 4 levels for 32-bit codes).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -42,7 +49,7 @@ constexpr int kThreads = 256;
 constexpr uint32_t kMultiOff = 0;                                        // uint32[1024]
 constexpr uint32_t kCountOff = kMultiOff + 4u * (1u << DF11_MULTI_BITS);  // uint16[4096]
 constexpr uint32_t kLutOff = kCountOff + 2u * (1u << DF11_COUNT_BITS);    // uint16[n][256]
-constexpr uint32_t kBadCount = 1u << 20;  // added to a thread's count when its window is corrupt
+constexpr uint32_t kBadCount = 1u << 20;  // added to a window's count when it is corrupt
 
 struct KArgs {
     const uint8_t *stream;
@@ -57,119 +64,214 @@ struct KArgs {
     uint32_t tile0, n_tiles;  // tiles [tile0, tile0 + n_tiles) of the unit
     uint32_t table_bytes;
     uint32_t ebuf_off;        // LDS byte offset of the exponent staging buffer
-    uint32_t exp_cap;         // its size in bytes
+    uint32_t exp_cap;         // its size in bytes; 4 trash bytes per thread follow
     uint32_t n_luts;
     uint32_t out_lo, out_hi, out_shift;
 };
 
-// Hierarchical walk for one code at the head of a left-aligned 32-bit window.
-// Returns (length << 8) | symbol, or 0 when no leaf is reached in 4 levels.
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Hierarchical walk for one code at the head of a left-aligned 32-bit window,
+// without branches.  Returns (length << 8) | symbol, or 0 when no leaf is
+// reached in 4 levels.
 __device__ __forceinline__ uint32_t walk_tables(const uint16_t *lut, uint32_t n_luts,
                                                 uint32_t w32) {
     uint32_t e = lut[w32 >> 24];
-    if (e & 0x8000u) {
 #pragma unroll
-        for (int lvl = 1; lvl < 4; lvl++) {
-            const uint32_t tbl = min(e & 0x7FFFu, n_luts - 1);
-            e = lut[(tbl << 8) | ((w32 >> (24 - 8 * lvl)) & 0xFFu)];
-            if (!(e & 0x8000u)) break;
-        }
-        if (e & 0x8000u) e = 0;
+    for (int lvl = 1; lvl < 4; lvl++) {
+        const uint32_t tbl = min(e & 0x7FFFu, n_luts - 1);
+        const uint32_t next = lut[(tbl << 8) | ((w32 >> (24 - 8 * lvl)) & 0xFFu)];
+        e = (e & 0x8000u) ? next : e;
     }
-    return e & 0x3FFFu;
+    return (e & 0x8000u) ? 0u : (e & 0x3FFFu);
 }
 
-// The 32 stream bits starting p bits into segment s of the window, for
-// p % 32 in [0, 32): alignbit((hi:lo) >> 1, 31 - p % 32).  a = hi >> 1 and
-// b = alignbit(hi, lo, 1) are formed once per segment.
-template <int B>
-struct Window {
-    uint32_t a[B / 4], b[B / 4];
-    __device__ __forceinline__ void init(const uint32_t (&d)[B / 4 + 1]) {
-#pragma unroll
-        for (int s = 0; s < B / 4; s++) {
-            a[s] = d[s] >> 1;
-            b[s] = __builtin_amdgcn_alignbit(d[s], d[s + 1], 1);
+// A multi-symbol entry for a code whose first code is longer than the index.
+__device__ __forceinline__ uint32_t long_entry(const uint16_t *lut, uint32_t n_luts,
+                                               uint32_t w32) {
+    const uint32_t le = walk_tables(lut, n_luts, w32);
+    const uint32_t len = (le >> 8) ? (le >> 8) : 63u;  // 63: unreachable once phase 1 passed
+    return (1u << 30) | (len << 24) | (le & 0xFFu);
+}
+
+// Thread t's C windows: 8*C bytes plus the 4 bytes after them (big-endian
+// dwords once swapped), their gap bytes and the tile bounds.
+template <int C>
+struct TileIn {
+    uint32_t d[2 * C + 1];
+    uint32_t gaps;  // gap of window c in byte c
+    uint32_t bounds;
+    __device__ __forceinline__ void load(const KArgs &a, uint32_t tile, uint32_t t) {
+        const uint64_t win0 = uint64_t(tile) * (kThreads * C) + uint64_t(C) * t;
+        const uint8_t *wp = a.stream + win0 * 8;
+        if constexpr (C == 1) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(wp);
+            d[0] = v.x;
+            d[1] = v.y;
+            gaps = a.gaps[win0];
+        } else {
+            static_assert(C == 2, "one or two windows per thread");
+            const uint4 v = *reinterpret_cast<const uint4 *>(wp);
+            d[0] = v.x;
+            d[1] = v.y;
+            d[2] = v.z;
+            d[3] = v.w;
+            gaps = *reinterpret_cast<const uint16_t *>(a.gaps + win0);
         }
-    }
-    // q = ~p: the shift 31 - p % 32 is q mod 32
-    __device__ __forceinline__ uint32_t at(int s, uint32_t q) const {
-        return __builtin_amdgcn_alignbit(a[s], b[s], q);
-    }
-    // any p < 64, segment chosen at run time (used for two codes per tile)
-    __device__ __forceinline__ uint32_t at_low(uint32_t p) const {
-        const uint32_t w0 = __builtin_amdgcn_alignbit(a[0], b[0], ~p);
-        const uint32_t w1 = __builtin_amdgcn_alignbit(a[1], b[1], ~p);
-        return p < 32 ? w0 : w1;
+        d[2 * C] = *reinterpret_cast<const uint32_t *>(wp + 8 * C);
+        bounds = a.bop[tile + (t & 1u)];
     }
 };
 
-// A multi-symbol step at window bits w32: the table entry, or for a first
-// code longer than the index, an entry built from the hierarchical walk.
-// Entry: bits 31..30 count, 29..24 total length, 23..0 symbols.
-__device__ __forceinline__ uint32_t multi_step(const uint8_t *fast, const uint16_t *lut,
-                                               uint32_t n_luts, uint32_t w32) {
-    uint32_t e = *reinterpret_cast<const uint32_t *>(
-        fast + kMultiOff + ((w32 >> (32 - DF11_MULTI_BITS)) << 2));
-    if (e < (1u << 30)) {
-        const uint32_t le = walk_tables(lut, n_luts, w32);
-        uint32_t len = le >> 8;
-        if (len == 0) len = 63;  // unreachable once phase 1 accepted the tile
-        e = (1u << 30) | (len << 24) | (le & 0xFFu);
-    }
-    return e;
-}
-
-// Phase 1: number of codes whose first bit lies in [gap, lim) of the window.
-// The loop carries q = ~p (alignbit takes 31 - p % 32 = ~p mod 32 directly).
-template <int B>
-__device__ __forceinline__ uint32_t count_codes(const Window<B> &W, uint32_t gap, uint32_t lim,
-                                                const uint8_t *fast, const uint16_t *lut,
-                                                uint32_t n_luts) {
-    uint32_t q = ~gap, cnt = 0;
-    const uint32_t lim1 = lim + 1;  // lim - p == lim1 + q
+// The 32 stream bits starting p bits into segment s (p % 32) of window c:
+// alignbit((hi:lo) >> 1, 31 - p % 32), valid for every p % 32 including 0,
+// with a = hi >> 1 and b = alignbit(hi, lo, 1) formed once per tile.  The
+// decode loops carry q = ~p, and 31 - p % 32 is q mod 32.
+template <int C>
+struct Windows {
+    uint32_t a[C][2], b[C][2];
+    __device__ __forceinline__ void init(const uint32_t (&d)[2 * C + 1]) {
 #pragma unroll
-    for (int s = 0; s < B / 4; s++) {
-        const uint32_t qend = ~min(32u * (s + 1), lim);  // p < end  <=>  q > ~end
-        while (q > qend) {
-            const uint32_t w32 = W.at(s, q);
-            const uint32_t e = *reinterpret_cast<const uint16_t *>(
-                fast + kCountOff + ((w32 >> (32 - DF11_COUNT_BITS)) << 1));
-            uint32_t adv = e >> 12;
-            uint32_t m = __builtin_amdgcn_ubfe(e, 0, min(lim1 + q, uint32_t(DF11_COUNT_BITS)));
-            if (adv == 0) {  // first code longer than the index
-                adv = walk_tables(lut, n_luts, w32) >> 8;
-                m = 1;
-                if (adv == 0) {  // no code here: corrupt stream or tables
-                    adv = 8 * B;
-                    cnt += kBadCount;
+        for (int c = 0; c < C; c++)
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+                a[c][s] = d[2 * c + s] >> 1;
+                b[c][s] = __builtin_amdgcn_alignbit(d[2 * c + s], d[2 * c + s + 1], 1);
+            }
+    }
+    __device__ __forceinline__ uint32_t at(int c, int s, uint32_t q) const {
+        return __builtin_amdgcn_alignbit(a[c][s], b[c][s], q);
+    }
+    __device__ __forceinline__ uint32_t at_low(int c, uint32_t p) const {  // any p < 64
+        return p < 32 ? at(c, 0, ~p) : at(c, 1, ~p);
+    }
+};
+
+// Phase 1: cnt[c] = number of codes whose first bit lies in [gap_c, lim_c).
+template <int C>
+__device__ __forceinline__ void count_codes(const Windows<C> &W, const uint32_t (&gap)[C],
+                                            const uint32_t (&lim)[C], const uint8_t *fast,
+                                            const uint16_t *lut, uint32_t n_luts,
+                                            uint32_t (&cnt)[C]) {
+    uint32_t q[C];
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        q[c] = ~gap[c];
+        cnt[c] = 0;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+        uint32_t qend[C];
+#pragma unroll
+        for (int c = 0; c < C; c++) qend[c] = ~min(32u * (s + 1), lim[c]);  // p < end <=> q > ~end
+        for (;;) {
+            bool act[C];
+            uint64_t any = 0;
+#pragma unroll
+            for (int c = 0; c < C; c++) {
+                act[c] = q[c] > qend[c];
+                any |= ballot(act[c]);
+            }
+            if (!any) break;
+            uint32_t w32[C], adv[C], m[C];
+            uint64_t longc = 0;
+#pragma unroll
+            for (int c = 0; c < C; c++) {
+                w32[c] = W.at(c, s, q[c]);
+                const uint32_t e = *reinterpret_cast<const uint16_t *>(
+                    fast + kCountOff + ((w32[c] >> (32 - DF11_COUNT_BITS)) << 1));
+                // only starts before lim count (lim - p == lim + 1 + q); an inactive
+                // chain counts nothing and does not move
+                const uint32_t cut = min(lim[c] + 1 + q[c], uint32_t(DF11_COUNT_BITS));
+                m[c] = __builtin_amdgcn_ubfe(e, 0, act[c] ? cut : 0u);
+                adv[c] = e >> 12;
+                longc |= ballot(adv[c] == 0);  // inactive lanes only cost a rare detour
+            }
+            if (longc) {  // rare: a first code longer than the count index
+#pragma unroll
+                for (int c = 0; c < C; c++) {
+                    const uint32_t len = walk_tables(lut, n_luts, w32[c]) >> 8;
+                    const bool here = act[c] && adv[c] == 0;
+                    cnt[c] += (here && len == 0) ? kBadCount : 0u;  // no code: corrupt input
+                    m[c] = here ? 1u : m[c];
+                    adv[c] = here ? (len ? len : 64u) : adv[c];
                 }
             }
-            cnt += __builtin_popcount(m);
-            q -= adv;
+#pragma unroll
+            for (int c = 0; c < C; c++) {
+                cnt[c] += uint32_t(__builtin_popcount(m[c]));
+                q[c] -= act[c] ? adv[c] : 0u;
+            }
         }
     }
-    return cnt;
 }
 
-// Phase 2: exponents of the window's codes to dst[0 ..), up to 2 bytes beyond.
-template <int B>
-__device__ __forceinline__ void decode_codes(const Window<B> &W, uint32_t gap, uint32_t lim,
-                                             const uint8_t *fast, const uint16_t *lut,
-                                             uint32_t n_luts, uint8_t *dst) {
-    uint32_t q = ~gap;
+// Phase 2: exponents of window c's codes to stage[dst[c] ..), up to 2 bytes
+// beyond.  Positions are byte offsets into the LDS array, not pointers: a
+// select between pointers held in registers loses the address space and
+// turns the stores into flat (vector memory) stores.
+template <int C>
+__device__ __forceinline__ void decode_codes(const Windows<C> &W, const uint32_t (&gap)[C],
+                                             const uint32_t (&lim)[C], const uint8_t *fast,
+                                             const uint16_t *lut, uint32_t n_luts,
+                                             uint8_t *stage, uint32_t (&dst)[C],
+                                             uint32_t trash) {
+    uint32_t q[C];
 #pragma unroll
-    for (int s = 0; s < B / 4; s++) {
-        const uint32_t qend = ~min(32u * (s + 1), lim);
-        while (q > qend) {
-            const uint32_t e = multi_step(fast, lut, n_luts, W.at(s, q));
-            dst[0] = uint8_t(e);
-            dst[1] = uint8_t(e >> 8);
-            dst[2] = uint8_t(e >> 16);
-            dst += e >> 30;
-            q -= (e >> 24) & 0x3Fu;
+    for (int c = 0; c < C; c++) q[c] = ~gap[c];
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+        uint32_t qend[C];
+#pragma unroll
+        for (int c = 0; c < C; c++) qend[c] = ~min(32u * (s + 1), lim[c]);
+        for (;;) {
+            bool act[C];
+            uint64_t any = 0;
+#pragma unroll
+            for (int c = 0; c < C; c++) {
+                act[c] = q[c] > qend[c];
+                any |= ballot(act[c]);
+            }
+            if (!any) break;
+            uint32_t w32[C], e[C];
+            uint64_t longc = 0;
+#pragma unroll
+            for (int c = 0; c < C; c++) {
+                w32[c] = W.at(c, s, q[c]);
+                e[c] = *reinterpret_cast<const uint32_t *>(
+                    fast + kMultiOff + ((w32[c] >> (32 - DF11_MULTI_BITS)) << 2));
+                longc |= ballot(e[c] < (1u << 30));  // inactive lanes only cost a rare detour
+            }
+            if (longc) {  // rare: a first code longer than 10 bits
+#pragma unroll
+                for (int c = 0; c < C; c++) {
+                    const uint32_t le = long_entry(lut, n_luts, w32[c]);
+                    e[c] = (e[c] < (1u << 30)) ? le : e[c];
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < C; c++) {
+                const uint32_t o = act[c] ? dst[c] : trash;
+                stage[o] = uint8_t(e[c]);
+                stage[o + 1] = uint8_t(e[c] >> 8);
+                stage[o + 2] = uint8_t(e[c] >> 16);
+                const uint32_t ea = act[c] ? e[c] : 0u;  // an inactive chain does not move
+                dst[c] += ea >> 30;
+                q[c] -= (ea >> 24) & 0x3Fu;
+            }
         }
     }
+}
+
+// The multi-symbol entry at bit p (< 64) of window c, long codes resolved.
+template <int C>
+__device__ __forceinline__ uint32_t entry_at(const Windows<C> &W, int c, uint32_t p,
+                                             const uint8_t *fast, const uint16_t *lut,
+                                             uint32_t n_luts) {
+    const uint32_t w32 = W.at_low(c, p);
+    const uint32_t e = *reinterpret_cast<const uint32_t *>(
+        fast + kMultiOff + ((w32 >> (32 - DF11_MULTI_BITS)) << 2));
+    return e < (1u << 30) ? long_entry(lut, n_luts, w32) : e;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -204,56 +306,39 @@ __device__ __forceinline__ void emit8(const KArgs &a, uint32_t gi, uint32_t lo, 
         uint4 v;
         assemble4(s8.x, e8.x, v.x, v.y);
         assemble4(s8.y, e8.y, v.z, v.w);
-        *reinterpret_cast<uint4 *>(a.out + (gi - a.out_shift)) = v;
+        // the output is not read again by this kernel: stream it past the caches
+        uint32_t *o = reinterpret_cast<uint32_t *>(a.out + (gi - a.out_shift));
+        __builtin_nontemporal_store(v.x, o);
+        __builtin_nontemporal_store(v.y, o + 1);
+        __builtin_nontemporal_store(v.z, o + 2);
+        __builtin_nontemporal_store(v.w, o + 3);
     } else if (gi + 8 > lo && gi < hi) {
+        // a tile's first or last chunk: the sm bytes are already in registers
+        // (re-reading them from memory would put serial round trips in front
+        // of the next barrier)
+#pragma unroll
         for (uint32_t k = 0; k < 8; k++) {
             const uint32_t i = gi + k;
-            if (i >= lo && i < hi) a.out[i - a.out_shift] = assemble1(a.sm[i], ex[k]);
+            const uint32_t sk = ((k < 4 ? s8.x : s8.y) >> (8 * (k & 3))) & 0xFFu;
+            if (i >= lo && i < hi) a.out[i - a.out_shift] = assemble1(sk, ex[k]);
         }
     }
 }
 
-// Per-tile inputs, loaded one tile ahead.  The tile bounds come through a
-// vector load (lane l reads block_out_pos[tile + (l & 1)]): a scalar load
-// would share its wait counter with LDS and stall the decode loops.
-template <int T, int B>
-struct TileIn {
-    uint32_t d[B / 4 + 1];
-    uint32_t gap, bounds;
-    __device__ __forceinline__ void load(const KArgs &a, uint32_t tile, uint32_t t) {
-        const uint64_t win = uint64_t(tile) * T + t;
-        const uint8_t *wp = a.stream + win * B;
-        if constexpr (B == 8) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(wp);
-            d[0] = v.x;
-            d[1] = v.y;
-        } else {
-            const uint4 v = *reinterpret_cast<const uint4 *>(wp);
-            d[0] = v.x;
-            d[1] = v.y;
-            d[2] = v.z;
-            d[3] = v.w;
-        }
-        d[B / 4] = *reinterpret_cast<const uint32_t *>(wp + B);
-        gap = a.gaps[win];
-        bounds = a.bop[tile + (t & 1u)];
-    }
-};
-
-template <int T, int B, int JP>
-__global__ __launch_bounds__(T) void df11_decode(KArgs a) {
+template <int C, int JP>
+__global__ __launch_bounds__(kThreads) void df11_decode(KArgs a) {
     // The fixed-size fast tables are the kernel's only static LDS, at address
     // 0, so their offsets fold into the LDS instructions' immediate offsets.
-    // Dynamic LDS: hierarchical tables, 16 bytes of wave totals, staging.
+    // Dynamic LDS: hierarchical tables, 16 bytes of wave totals, staging, trash.
     __shared__ __align__(16) uint8_t fast[kLutOff];
     extern __shared__ __align__(16) uint8_t dyn[];
-    static_assert(T == 256, "the block scan reads the 4 wave totals as one uint4");
+    constexpr uint32_t W = kThreads * C;  // windows per tile
     const uint32_t t = threadIdx.x, lane = t & 63u, wid = t >> 6;
     if (blockIdx.x >= a.n_tiles) return;
 
-    TileIn<T, B> cur;
+    TileIn<C> cur;
     cur.load(a, a.tile0 + blockIdx.x, t);
-    for (uint32_t i = 16 * t; i < a.table_bytes; i += 16 * T) {
+    for (uint32_t i = 16 * t; i < a.table_bytes; i += 16 * kThreads) {
         const uint4 v = *reinterpret_cast<const uint4 *>(a.tables + i);
         *reinterpret_cast<uint4 *>(i < kLutOff ? fast + i : dyn + (i - kLutOff)) = v;
     }
@@ -261,6 +346,7 @@ __global__ __launch_bounds__(T) void df11_decode(KArgs a) {
     const uint16_t *lut = reinterpret_cast<const uint16_t *>(dyn);
     uint32_t *wave_sum = reinterpret_cast<uint32_t *>(dyn + a.ebuf_off - 16);
     uint8_t *ebuf = dyn + a.ebuf_off;
+    const uint32_t trash = a.exp_cap + 4 * t;  // offsets below are relative to ebuf
 
     for (uint32_t it = blockIdx.x; it < a.n_tiles; it += gridDim.x) {
         const uint32_t tile = a.tile0 + it;
@@ -273,27 +359,33 @@ __global__ __launch_bounds__(T) void df11_decode(KArgs a) {
         uint2 smv[JP];
 #pragma unroll
         for (int j = 0; j < JP; j++) {
-            const uint32_t c = t + j * T;
+            const uint32_t c = t + j * kThreads;
             if (c < n8) smv[j] = *reinterpret_cast<const uint2 *>(a.sm + A0 + 8 * c);
         }
-        // next tile's inputs, issued before this tile's stores so that waiting
-        // for them never waits for those stores
-        TileIn<T, B> nxt;
+        // next tile's inputs, issued before this tile's stores
+        TileIn<C> nxt;
         nxt.load(a, a.tile0 + min(it + gridDim.x, a.n_tiles - 1), t);
 
-        uint32_t d[B / 4 + 1];
+        uint32_t d[2 * C + 1];
 #pragma unroll
-        for (int k = 0; k <= B / 4; k++) d[k] = __builtin_bswap32(cur.d[k]);
-        Window<B> W;
-        W.init(d);
-        const uint32_t gap = cur.gap;
-        const uint64_t base = (uint64_t(tile) * T + t) * (8 * B);
-        const uint32_t lim =
-            a.total_bits > base ? uint32_t(min<uint64_t>(8 * B, a.total_bits - base)) : 0u;
+        for (int k = 0; k <= 2 * C; k++) d[k] = __builtin_bswap32(cur.d[k]);
+        Windows<C> win;
+        win.init(d);
+        uint32_t gap[C], lim[C];
+#pragma unroll
+        for (int c = 0; c < C; c++) {
+            gap[c] = (cur.gaps >> (8 * c)) & 0xFFu;
+            const uint64_t base = (uint64_t(tile) * W + uint64_t(C) * t + c) * 64;
+            lim[c] = a.total_bits > base ? uint32_t(min<uint64_t>(64, a.total_bits - base)) : 0u;
+        }
 
         // phase 1 and the block scan
-        const uint32_t cnt = count_codes<B>(W, gap, lim, fast, lut, a.n_luts);
-        const uint32_t incl = wave_inclusive_scan(cnt);
+        uint32_t cnt[C];
+        count_codes<C>(win, gap, lim, fast, lut, a.n_luts, cnt);
+        uint32_t mine_total = 0;
+#pragma unroll
+        for (int c = 0; c < C; c++) mine_total += cnt[c];
+        const uint32_t incl = wave_inclusive_scan(mine_total);
         if (lane == 63) wave_sum[wid] = incl;
         __syncthreads();
         const uint4 ws = *reinterpret_cast<const uint4 *>(wave_sum);
@@ -308,18 +400,26 @@ __global__ __launch_bounds__(T) void df11_decode(KArgs a) {
         }
 
         // phase 2, then repair the two bytes a neighbour's last step may have spilled onto
-        uint8_t *mine = ebuf + (P0 - A0) + before + incl - cnt;
-        decode_codes<B>(W, gap, lim, fast, lut, a.n_luts, mine);
+        uint32_t first[C], dst[C];
+        first[0] = (P0 - A0) + before + incl - mine_total;
+#pragma unroll
+        for (int c = 1; c < C; c++) first[c] = first[c - 1] + cnt[c - 1];
+#pragma unroll
+        for (int c = 0; c < C; c++) dst[c] = first[c];
+        decode_codes<C>(win, gap, lim, fast, lut, a.n_luts, ebuf, dst, trash);
         __syncthreads();
-        if (cnt) {
-            uint32_t e = multi_step(fast, lut, a.n_luts, W.at_low(gap));
-            mine[0] = uint8_t(e);
-            if (cnt > 1) {
-                if ((e >> 30) < 2)
-                    e = multi_step(fast, lut, a.n_luts, W.at_low(gap + ((e >> 24) & 0x3Fu)));
-                else
-                    e >>= 8;
-                mine[1] = uint8_t(e);
+#pragma unroll
+        for (int c = 0; c < C; c++) {
+            if (cnt[c]) {
+                uint32_t e = entry_at<C>(win, c, gap[c], fast, lut, a.n_luts);
+                ebuf[first[c]] = uint8_t(e);
+                if (cnt[c] > 1) {
+                    if ((e >> 30) < 2)
+                        e = entry_at<C>(win, c, gap[c] + ((e >> 24) & 0x3Fu), fast, lut, a.n_luts);
+                    else
+                        e >>= 8;
+                    ebuf[first[c] + 1] = uint8_t(e);
+                }
             }
         }
         __syncthreads();
@@ -328,10 +428,10 @@ __global__ __launch_bounds__(T) void df11_decode(KArgs a) {
         const uint32_t lo = max(P0, a.out_lo), hi = min(P1, a.out_hi);
 #pragma unroll
         for (int j = 0; j < JP; j++) {
-            const uint32_t c = t + j * T;
+            const uint32_t c = t + j * kThreads;
             if (c < n8) emit8(a, A0 + 8 * c, lo, hi, smv[j], ebuf + 8 * c);
         }
-        for (uint32_t c = t + JP * T; c < n8; c += T)
+        for (uint32_t c = t + JP * kThreads; c < n8; c += kThreads)
             emit8(a, A0 + 8 * c, lo, hi, *reinterpret_cast<const uint2 *>(a.sm + A0 + 8 * c),
                   ebuf + 8 * c);
         cur = nxt;
@@ -340,27 +440,28 @@ __global__ __launch_bounds__(T) void df11_decode(KArgs a) {
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
-template <int B>
-const void *kernel_for() {
-    return reinterpret_cast<const void *>(&df11_decode<kThreads, B, (B == 8 ? 4 : 8)>);
+const void *kernel_for(uint32_t tile_windows) {
+    return tile_windows == 256 ? reinterpret_cast<const void *>(&df11_decode<1, 4>)
+                               : reinterpret_cast<const void *>(&df11_decode<2, 8>);
 }
 
 // Checks shared by both entry points; fills the launch-independent fields.
 int prepare(const df11_device_stream *s, KArgs &a) {
     if (!s) return DF11_E_INVALID;
-    if (s->threads != kThreads || (s->bytes_per_thread != 8 && s->bytes_per_thread != 16))
+    if (s->window_bytes != 8 || (s->tile_windows != 256 && s->tile_windows != 512))
         return DF11_E_INVALID;
     if (s->n_weights >= (uint64_t(1) << 32)) return DF11_E_INVALID;
-    const uint64_t tile_bits = uint64_t(8) * s->bytes_per_thread * s->threads;
+    const uint64_t tile_bits = uint64_t(64) * s->tile_windows;
     if (s->n_tiles != (s->total_bits + tile_bits - 1) / tile_bits) return DF11_E_INVALID;
     if (s->n_tiles >= (uint64_t(1) << 32)) return DF11_E_INVALID;
     if (s->n_weights == 0) return DF11_OK;
     if (!s->stream || !s->sm || !s->gaps || !s->block_out_pos || !s->tables)
         return DF11_E_INVALID;
-    if (!aligned(s->stream, 16) || !aligned(s->sm, 16) || !aligned(s->tables, 16))
+    if (!aligned(s->stream, 16) || !aligned(s->sm, 16) || !aligned(s->tables, 16) ||
+        !aligned(s->gaps, 2))
         return DF11_E_INVALID;
     if (s->n_luts < 1 || s->n_luts > DF11_MAX_LUTS) return DF11_E_INVALID;
-    if (s->max_tile_symbols > 8u * s->bytes_per_thread * s->threads) return DF11_E_INVALID;
+    if (s->max_tile_symbols > 64u * s->tile_windows) return DF11_E_INVALID;
     a.stream = s->stream;
     a.sm = s->sm;
     a.gaps = s->gaps;
@@ -370,7 +471,7 @@ int prepare(const df11_device_stream *s, KArgs &a) {
     a.n_weights = uint32_t(s->n_weights);
     a.n_luts = s->n_luts;
     a.table_bytes = kLutOff + 512u * s->n_luts;
-    // dynamic LDS: hierarchical tables, 16 bytes of wave totals, then staging
+    // dynamic LDS: hierarchical tables, 16 bytes of wave totals, staging, trash
     a.ebuf_off = 512u * s->n_luts + 16;
     // outputs from P0 & ~7 to the last 8-chunk, plus the 2 spill bytes
     a.exp_cap = (s->max_tile_symbols + 7 + 16 + 15) & ~15u;
@@ -380,8 +481,8 @@ int prepare(const df11_device_stream *s, KArgs &a) {
 int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t st) {
     if (n_tiles == 0) return DF11_OK;
     a.n_tiles = n_tiles;
-    const size_t lds = size_t(a.ebuf_off) + a.exp_cap;
-    const void *fn = s->bytes_per_thread == 8 ? kernel_for<8>() : kernel_for<16>();
+    const size_t lds = size_t(a.ebuf_off) + a.exp_cap + 4 * kThreads;
+    const void *fn = kernel_for(s->tile_windows);
     if (lds > 65536 &&
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
         return DF11_E_INVALID;

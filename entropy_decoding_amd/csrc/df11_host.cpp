@@ -279,7 +279,7 @@ void build_multi_tables(df11_codebook *cb) {
     }
 }
 
-bool valid_layout(uint32_t T, uint32_t B) { return T == 256 && (B == 8 || B == 16); }
+bool valid_layout(uint32_t T, uint32_t B) { return B == 8 && (T == 256 || T == 512); }
 
 int log2u(uint64_t x) {
     int r = 0;
@@ -437,11 +437,11 @@ int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel, u
 }
 
 int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors, const uint64_t *numel,
-                     uint32_t n_tensors, uint32_t threads, uint32_t bytes_per_thread,
+                     uint32_t n_tensors, uint32_t tile_windows, uint32_t window_bytes,
                      df11_sizes *out) {
     try {
         if (!cb || !out || bad_inputs(tensors, numel, n_tensors) ||
-            !valid_layout(threads, bytes_per_thread) || !valid_codebook(cb))
+            !valid_layout(tile_windows, window_bytes) || !valid_codebook(cb))
             return DF11_E_INVALID;
         auto pieces = split(tensors, numel, n_tensors);
         std::vector<uint64_t> per;
@@ -449,18 +449,18 @@ int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors, co
         histogram(pieces, per, counts);
         uint64_t n = 0;
         for (uint32_t k = 0; k < n_tensors; k++) n += numel[k];
-        return sizes_from_counts(cb, counts, n, threads, bytes_per_thread, out);
+        return sizes_from_counts(cb, counts, n, tile_windows, window_bytes, out);
     } catch (...) {
         return DF11_E_INVALID;
     }
 }
 
 int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const uint64_t *numel,
-                uint32_t n_tensors, uint32_t threads, uint32_t bytes_per_thread,
+                uint32_t n_tensors, uint32_t tile_windows, uint32_t window_bytes,
                 df11_host_stream *out) {
     try {
         if (!cb || !out || bad_inputs(tensors, numel, n_tensors) ||
-            !valid_layout(threads, bytes_per_thread) || !valid_codebook(cb) ||
+            !valid_layout(tile_windows, window_bytes) || !valid_codebook(cb) ||
             out->n_tensors != n_tensors)
             return DF11_E_INVALID;
         auto pieces = split(tensors, numel, n_tensors);
@@ -471,7 +471,7 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const u
         for (uint32_t k = 0; k < n_tensors; k++) n += numel[k];
         if (n >= (uint64_t(1) << 32)) return DF11_E_INVALID;
         df11_sizes sz;
-        int rc = sizes_from_counts(cb, counts, n, threads, bytes_per_thread, &sz);
+        int rc = sizes_from_counts(cb, counts, n, tile_windows, window_bytes, &sz);
         if (rc != DF11_OK) return rc;
         if (!out->stream || !out->sm || !out->block_out_pos || !out->tensor_offsets ||
             (n_tensors && !out->tensor_tiles) || (sz.n_windows && !out->gaps))
@@ -487,8 +487,8 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const u
             for (int s = 0; s < kSyms; s++) b += per[p * kSyms + s] * cb->code_len[s];
             start[p + 1] = start[p] + b;
         }
-        const int wshift = log2u(uint64_t(8) * bytes_per_thread);
-        const int tshift = wshift + log2u(threads);
+        const int wshift = log2u(uint64_t(8) * window_bytes);
+        const int tshift = wshift + log2u(tile_windows);
 
         std::memset(out->stream, 0, sz.stream_bytes);
         std::memset(out->gaps, 255, sz.n_windows);
@@ -535,8 +535,8 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const u
         uint32_t mx = 0;
         for (uint64_t t = 0; t < sz.n_tiles; t++)
             mx = std::max(mx, out->block_out_pos[t + 1] - out->block_out_pos[t]);
-        out->threads = threads;
-        out->bytes_per_thread = bytes_per_thread;
+        out->tile_windows = tile_windows;
+        out->window_bytes = window_bytes;
         out->max_tile_symbols = mx;
         out->n_weights = n;
         out->total_bits = sz.total_bits;

@@ -22,8 +22,9 @@
  *   unit          the tensors compressed together under one codebook and
  *                 decompressed by one launch (a tensor, or all weight tensors
  *                 of one transformer block, concatenated in order)
- *   window        B consecutive stream bytes decoded by one GPU thread
- *   tile          T consecutive windows decoded by one workgroup
+ *   window        B = 8 consecutive stream bytes, decoded serially from its gap
+ *   tile          T consecutive windows decoded by one workgroup of 256 threads,
+ *                 T / 256 adjacent windows per thread
  *
  * Stream format.  Codes are canonical (symbols ordered by (length, value)
  * take consecutive codes), at most 32 bits long, and written MSB-first: bit j
@@ -130,8 +131,8 @@ typedef struct df11_host_stream {
     uint64_t stream_capacity, sm_capacity, gaps_capacity, bop_capacity;
     uint32_t n_tensors;
     /* results */
-    uint32_t threads;           /* T */
-    uint32_t bytes_per_thread;  /* B */
+    uint32_t tile_windows;      /* T */
+    uint32_t window_bytes;      /* B */
     uint32_t max_tile_symbols;  /* max over tiles of block_out_pos[t+1] - block_out_pos[t] */
     uint64_t n_weights;
     uint64_t total_bits;
@@ -158,8 +159,8 @@ typedef struct df11_device_stream {
     uint64_t total_bits;
     uint64_t n_tiles;
     uint32_t n_luts;
-    uint32_t threads;
-    uint32_t bytes_per_thread;
+    uint32_t tile_windows;
+    uint32_t window_bytes;
     uint32_t max_tile_symbols;
     uint32_t n_tensors;
 } df11_device_stream;
@@ -182,12 +183,12 @@ int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel,
 
 /*
  * df11_encode_size -- host.  Sizes of all arrays df11_encode will write for
- * these tensors under layout (threads T, bytes_per_thread B).  Supported
- * layouts: T = 256 with B = 8 or 16.  Errors: DF11_E_INVALID, DF11_E_SYMBOL.
+ * these tensors under layout (tile_windows T, window_bytes B).  Supported
+ * layouts: B = 8 with T = 256 or 512.  Errors: DF11_E_INVALID, DF11_E_SYMBOL.
  */
 int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors,
-                     const uint64_t *numel, uint32_t n_tensors, uint32_t threads,
-                     uint32_t bytes_per_thread, df11_sizes *out);
+                     const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
+                     uint32_t window_bytes, df11_sizes *out);
 
 /*
  * df11_encode -- host, offline.  Writes the concatenated exponent code stream,
@@ -199,8 +200,8 @@ int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors,
  * df11_encode_size figure), DF11_E_INVALID when N >= 2^32.
  */
 int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors,
-                const uint64_t *numel, uint32_t n_tensors, uint32_t threads,
-                uint32_t bytes_per_thread, df11_host_stream *out);
+                const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
+                uint32_t window_bytes, df11_host_stream *out);
 
 /*
  * df11_decompress_block -- device.  Transformer-block-level decompression

@@ -181,18 +181,18 @@ def encode(tensors, cb: Codebook) -> Encoded:
     return Encoded(stream[: (total + 7) // 8], sm, total, starts, numel)
 
 
-def aux(tensors, cb: Codebook, threads: int, bytes_per_thread: int, fast: bool = True):
-    """(gaps uint8[n_tiles*threads], block_out_pos uint32[n_tiles+1]) from the definitions."""
+def aux(tensors, cb: Codebook, tile_windows: int, window_bytes: int, fast: bool = True):
+    """(gaps uint8[n_tiles*tile_windows], block_out_pos uint32[n_tiles+1]) from the definitions."""
     w = _cat(tensors)
     lens = np.ascontiguousarray(cb.lens, dtype=np.uint8)
     total = int(sum(int(lens[e]) * int(c) for e, c in enumerate(histogram(w))))
-    window_bits = 8 * bytes_per_thread
-    tile_bits = window_bits * threads
+    window_bits = 8 * window_bytes
+    tile_bits = window_bits * tile_windows
     n_tiles = (total + tile_bits - 1) // tile_bits
-    gaps = np.zeros(n_tiles * threads, dtype=np.uint8)
+    gaps = np.zeros(n_tiles * tile_windows, dtype=np.uint8)
     bop = np.zeros(n_tiles + 1, dtype=np.uint32)
     f = lib().oracle_aux_fast if fast else lib().oracle_aux
-    r = f(_p(w, ctypes.c_uint16), w.size, _p(lens, ctypes.c_uint8), window_bits, threads,
+    r = f(_p(w, ctypes.c_uint16), w.size, _p(lens, ctypes.c_uint8), window_bits, tile_windows,
           _p(gaps, ctypes.c_uint8), gaps.size, _p(bop, ctypes.c_uint32), n_tiles)
     if r != 0:
         raise ValueError(f"oracle_aux failed ({r})")

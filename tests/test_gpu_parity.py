@@ -18,7 +18,7 @@ import entropy_decoding_amd as ed  # noqa: E402
 import oracle  # noqa: E402
 import synth_weights as sw  # noqa: E402
 
-T = 256
+B = 8  # window bytes
 
 
 def say(msg):
@@ -44,19 +44,19 @@ def _dev_i16(a):
 class Unit:
     """Library-compressed unit resident on the GPU."""
 
-    def __init__(self, tensors, bpt=8):
+    def __init__(self, tensors, tw=ed.DEFAULT_TILE_WINDOWS):
         self.tensors = [np.asarray(t, dtype=np.uint16).reshape(-1) for t in tensors]
         self.cb = ed.df11_build_codebook(self.tensors)
-        self.hs = ed.df11_encode(self.cb, self.tensors, T, bpt)
+        self.hs = ed.df11_encode(self.cb, self.tensors, tw, B)
         self.ds = ed.DeviceStream(self.hs, self.cb, "cuda")
         self.n = self.hs.n_weights
-        self.bpt = bpt
+        self.tw = tw
 
     def decompress(self, poison=-1, label=""):
         out = torch.full((max(self.n, 1),), poison, dtype=torch.int16, device="cuda")
         status = torch.zeros(1, dtype=torch.int32, device="cuda")
         say(f"[gpu] df11_decompress_block {label} N={self.n} tiles={self.hs.n_tiles} "
-            f"B={self.bpt} luts={self.cb.n_luts} max_len={self.cb.max_len}")
+            f"T={self.tw} luts={self.cb.n_luts} max_len={self.cb.max_len}")
         ed.df11_decompress_block(self.ds, out, status)
         torch.cuda.synchronize()
         return out[: self.n], int(status.item())
@@ -71,11 +71,10 @@ class Unit:
         return out[:nk], int(status.item())
 
     def tile_start_bit(self, t):
-        wb = 8 * self.bpt
-        g = self.hs.gaps[t * T:(t + 1) * T]
+        g = self.hs.gaps[t * self.tw:(t + 1) * self.tw]
         j = int(np.argmax(g != 255))
         assert g[j] != 255
-        return (t * T + j) * wb + int(g[j])
+        return (t * self.tw + j) * 8 * B + int(g[j])
 
     def oracle_tile(self, t):
         """The oracle's bit-serial decode of tile t of the library's stream."""
@@ -109,15 +108,15 @@ def check_sampled_tiles(u, out, n_samples=24, seed=0):
 # ------------------------------------------------------------------ small, exhaustive
 
 
-@pytest.mark.parametrize("bpt", [8, 16])
-def test_config0_every_output_equals_the_oracle(bpt, unit_tensors):
+@pytest.mark.parametrize("tw", [256, 512])
+def test_config0_every_output_equals_the_oracle(tw, unit_tensors):
     (w,) = unit_tensors("0")
     ocb = oracle.codebook(w)
     enc = oracle.encode(w, ocb)
     odec = oracle.decode(enc.stream, 0, enc.total_bits, ocb.lens, enc.sm)
-    u = Unit([w], bpt)
-    assert u.hs.n_tiles > 1 and u.hs.total_bits % (8 * T * bpt) != 0  # ragged last tile
-    out, st = u.decompress(-1, f"cfg0 B={bpt}")
+    u = Unit([w], tw)
+    assert u.hs.n_tiles > 1 and u.hs.total_bits % (8 * B * tw) != 0  # ragged last tile
+    out, st = u.decompress(-1, f"cfg0 T={tw}")
     assert st == 0
     got = out.cpu().numpy().view(np.uint16)
     assert np.array_equal(got, odec)
@@ -136,8 +135,7 @@ def test_random_multi_tensor_units(seed):
         tensors.append(z.astype(np.uint16))
     if sum(t.size for t in tensors) == 0:
         tensors.append(np.array([0x3F80], dtype=np.uint16))
-    bpt = 8 if seed % 3 else 16
-    u = Unit(tensors, bpt)
+    u = Unit(tensors, 512 if seed % 3 else 256)
     out = check_identity(u, f"random seed={seed}")
     check_sampled_tiles(u, out, 8, seed)
     offs = u.hs.tensor_offsets
@@ -164,7 +162,7 @@ def test_single_exponent_one_bit_codes():
     w = (np.arange(300_000, dtype=np.uint32) * 2654435761 % 65536).astype(np.uint16)
     w = (w & np.uint16(0x807F)) | np.uint16(121 << 7)
     u = Unit([w])
-    assert u.hs.max_tile_symbols == 8 * 8 * T
+    assert u.hs.max_tile_symbols == 8 * B * u.tw
     check_identity(u, "single exponent")
 
 
@@ -221,7 +219,7 @@ def test_corrupt_gap_is_reported(unit_tensors):
     (w,) = unit_tensors("0")
     u = Unit([w])
     gaps = u.hs.gaps.copy()
-    gaps[3 * T + 17] = 255  # a window whose codes are now skipped
+    gaps[3 * u.tw + 17] = 255  # a window whose codes are now skipped
     u.ds.gaps.copy_(torch.from_numpy(gaps))
     _, st = u.decompress(-1, "corrupt gap")
     assert st == ed.DF11_E_CORRUPT
@@ -246,7 +244,7 @@ def test_invalid_arguments_are_rejected_before_launch(unit_tensors):
 
 def test_empty_unit_launches_nothing():
     d = ed.df11_device_stream()
-    d.threads, d.bytes_per_thread = 256, 8
+    d.tile_windows, d.window_bytes = 512, 8
     rc = ed.LIB.df11_decompress_block(ed.ctypes.byref(d), None, None, None)
     assert rc == ed.DF11_OK
 

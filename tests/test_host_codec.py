@@ -13,7 +13,7 @@ import entropy_decoding_amd as ed
 import oracle
 
 
-def _compare(tensors, threads=256, bpt=8, expect_same_lengths=True):
+def _compare(tensors, threads=512, bpt=8, expect_same_lengths=True):
     cb = ed.df11_build_codebook(tensors)
     lens, codes = ed.codebook_arrays(cb)
     ocb = oracle.codebook(tensors)
@@ -64,8 +64,8 @@ def test_stress_configs_match_oracle(unit_tensors, cfg):
     _compare([w[: 1 << 22]])
 
 
-def test_b16_layout_matches_oracle(unit_tensors):
-    _compare(unit_tensors("0"), bpt=16)
+def test_256_window_tiles_match_oracle(unit_tensors):
+    _compare(unit_tensors("0"), threads=256)
 
 
 def test_multi_tensor_unit_with_ragged_and_empty_tensors():
@@ -151,7 +151,7 @@ def test_errors():
         ed.df11_encode(cb, [other])
     assert e.value.status == ed.DF11_E_SYMBOL
     with pytest.raises(ed.Df11Error) as e:
-        ed.df11_encode(cb, [w], threads=128)
+        ed.df11_encode(cb, [w], tile_windows=128)
     assert e.value.status == ed.DF11_E_INVALID
     with pytest.raises(ed.Df11Error) as e:
         ed.df11_build_codebook([np.zeros(0, dtype=np.uint16)])

@@ -197,7 +197,7 @@ def test_uniform_256_exponents_stream_is_the_exponent_bytes():
     assert np.array_equal(cb.codes, np.arange(256, dtype=np.uint32))
     enc = oracle.encode(w, cb)
     assert np.array_equal(enc.stream, e.astype(np.uint8))
-    gaps, bop = oracle.aux(w, cb, threads=4, bytes_per_thread=8)
+    gaps, bop = oracle.aux(w, cb, tile_windows=4, window_bytes=8)
     assert (gaps == 0).all()
     assert np.array_equal(bop, np.minimum(np.arange(bop.size) * 32, e.size).astype(np.uint32))
 
