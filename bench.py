@@ -167,7 +167,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="2")
     ap.add_argument("--tile-windows", type=int, default=256, choices=(256, 512))
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -7,8 +7,11 @@
 // transformer-block-level launches; the output is bit-identical BF16.  The
 // kernel's organisation is this library's own, for CDNA4:
 //
-// * A persistent grid (as many workgroups as fit on the device at once) walks
-//   the tiles; each workgroup copies the tables into LDS once.  A tile is
+// * Each workgroup copies the tables into LDS once and then walks about 8
+//   tiles, grid-stride; the grid is the larger of the device's resident
+//   capacity and n_tiles / 8.  Many short-lived workgroups measured faster
+//   than a resident-only grid (0.62 vs 0.65 ms on the 70B block): their
+//   dispatch order keeps the addresses in flight compact.  A tile is
 //   256*C windows of 8 bytes; thread t decodes windows C*t .. C*t + C - 1 as
 //   C independent dependency chains, so each LDS lookup latency is shared by C
 //   codes in flight.
@@ -50,6 +53,7 @@ constexpr uint32_t kMultiOff = 0;                                        // uint
 constexpr uint32_t kCountOff = kMultiOff + 4u * (1u << DF11_MULTI_BITS);  // uint16[4096]
 constexpr uint32_t kLutOff = kCountOff + 2u * (1u << DF11_COUNT_BITS);    // uint16[n][256]
 constexpr uint32_t kBadCount = 1u << 20;  // added to a window's count when it is corrupt
+constexpr uint32_t kTilesPerWorkgroup = 8;
 
 struct KArgs {
     const uint8_t *stream;
@@ -492,7 +496,10 @@ int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t 
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess)
         return DF11_E_HIP;
     if (per_cu < 1) return DF11_E_INVALID;
-    const uint32_t grid = uint32_t(std::min<uint64_t>(n_tiles, uint64_t(cus) * per_cu));
+    const uint64_t resident = uint64_t(cus) * per_cu;
+    const uint64_t want =
+        std::max<uint64_t>(resident, (n_tiles + kTilesPerWorkgroup - 1) / kTilesPerWorkgroup);
+    const uint32_t grid = uint32_t(std::min<uint64_t>(n_tiles, want));
     void *args[] = {&a};
     const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, lds, st);
     return e == hipSuccess ? DF11_OK : DF11_E_HIP;
