@@ -7,11 +7,14 @@
 // transformer-block-level launches; the output is bit-identical BF16.  The
 // kernel's organisation is this library's own, for CDNA4:
 //
-// * Each workgroup copies the tables into LDS once and then walks about 8
+// * Each workgroup copies the tables into LDS once and then walks about 4
 //   tiles, grid-stride; the grid is the larger of the device's resident
-//   capacity and n_tiles / 8.  Many short-lived workgroups measured faster
+//   capacity and n_tiles / 4.  Many short-lived workgroups measured faster
 //   than a resident-only grid (0.62 vs 0.65 ms on the 70B block): their
-//   dispatch order keeps the addresses in flight compact.  A tile is
+//   dispatch order keeps the addresses in flight compact.  Occupancy
+//   matters: on the 70B block, 6, 5 and 4 workgroups per CU measured 5%,
+//   14% and 33% slower than 7; the LDS budget (fast tables, hierarchical
+//   tables 1.., staging) stays near 20 KiB so that 7-8 fit.  A tile is
 //   256*C windows of 8 bytes; thread t decodes windows C*t .. C*t + C - 1 as
 //   C independent dependency chains, so each LDS lookup latency is shared by C
 //   codes in flight.
@@ -32,14 +35,14 @@
 //   into an LDS staging buffer at their offsets.  A step writes all 3 slots,
 //   so a window's last step may spill up to 2 bytes onto the next window's
 //   first two outputs; every window rewrites those after a barrier.
-// * The decode loops are wave-uniform: they run until no lane has work
-//   (ballot), finished chains are masked by selects and their writes go to
-//   the lane's own trash slot (stores from many lanes to one address would be
-//   serialised), so no exec-mask bookkeeping sits in the dependency chain.
+// * The decode loops run until no lane of the wave has work (ballot); lanes
+//   whose chain has finished are masked off for the update, so they neither
+//   count, write nor move.
 // * The outputs are assembled 8 at a time from 8 sm bytes and 8 exponent
 //   bytes with byte permutes; the lanes of a wave store 1 KiB contiguously.
 // Codes longer than the fast tables' index walk the hierarchical 8-bit
-// tables (up to 4 levels for 32-bit codes).
+// tables from level 1 (the fast entry names the level-1 table), up to level
+// 3 for 32-bit codes.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -53,7 +56,7 @@ constexpr uint32_t kMultiOff = 0;                                        // uint
 constexpr uint32_t kCountOff = kMultiOff + 4u * (1u << DF11_MULTI_BITS);  // uint16[4096]
 constexpr uint32_t kLutOff = kCountOff + 2u * (1u << DF11_COUNT_BITS);    // uint16[n][256]
 constexpr uint32_t kBadCount = 1u << 20;  // added to a window's count when it is corrupt
-constexpr uint32_t kTilesPerWorkgroup = 8;
+constexpr uint32_t kTilesPerWorkgroup = 4;
 
 struct KArgs {
     const uint8_t *stream;
@@ -66,34 +69,45 @@ struct KArgs {
     uint64_t total_bits;
     uint32_t n_weights;
     uint32_t tile0, n_tiles;  // tiles [tile0, tile0 + n_tiles) of the unit
-    uint32_t table_bytes;
-    uint32_t ebuf_off;        // LDS byte offset of the exponent staging buffer
-    uint32_t exp_cap;         // its size in bytes; 4 trash bytes per thread follow
-    uint32_t n_luts;
+    uint32_t lds_tables;      // bytes of the table image copied to LDS (all but the root)
+    uint32_t ebuf_off;        // dynamic-LDS byte offset of the exponent staging buffer
+    uint32_t exp_cap;         // its size in bytes
+    uint32_t lut_last;        // highest hierarchical table index held in LDS (>= 1)
     uint32_t out_lo, out_hi, out_shift;
 };
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
-// Hierarchical walk for one code at the head of a left-aligned 32-bit window,
-// without branches.  Returns (length << 8) | symbol, or 0 when no leaf is
-// reached in 4 levels.
-__device__ __forceinline__ uint32_t walk_tables(const uint16_t *lut, uint32_t n_luts,
-                                                uint32_t w32) {
-    uint32_t e = lut[w32 >> 24];
+typedef __attribute__((address_space(3))) uint8_t lds8;
+
+// The LDS address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return uint32_t(size_t((const lds8 *)p));
+}
+
+// Hierarchical walk, without branches, for a code longer than 8 bits at the
+// head of a left-aligned 32-bit window.  The walk starts at level 1: the fast
+// tables hold the index of the level-1 table that the root would point to, so
+// the root table never needs to be in LDS.  lut[(k - 1) * 256 + b] is entry b
+// of table k >= 1; last is the highest table index present (at least 1).
+// Returns (length << 8) | symbol, or 0 when no leaf is reached by level 3.
+__device__ __forceinline__ uint32_t walk_tables(const uint16_t *lut, uint32_t last,
+                                                uint32_t tbl, uint32_t w32) {
+    uint32_t e = 0x8000u | tbl;
 #pragma unroll
     for (int lvl = 1; lvl < 4; lvl++) {
-        const uint32_t tbl = min(e & 0x7FFFu, n_luts - 1);
-        const uint32_t next = lut[(tbl << 8) | ((w32 >> (24 - 8 * lvl)) & 0xFFu)];
+        const uint32_t k = min(max(e & 0x7FFFu, 1u), last);
+        const uint32_t next = lut[((k << 8) | ((w32 >> (24 - 8 * lvl)) & 0xFFu)) - 256u];
         e = (e & 0x8000u) ? next : e;
     }
     return (e & 0x8000u) ? 0u : (e & 0x3FFFu);
 }
 
-// A multi-symbol entry for a code whose first code is longer than the index.
-__device__ __forceinline__ uint32_t long_entry(const uint16_t *lut, uint32_t n_luts,
+// A multi-symbol entry for a window whose first code is longer than the
+// index; e is the fast-table entry, which holds the level-1 table index.
+__device__ __forceinline__ uint32_t long_entry(const uint16_t *lut, uint32_t last, uint32_t e,
                                                uint32_t w32) {
-    const uint32_t le = walk_tables(lut, n_luts, w32);
+    const uint32_t le = walk_tables(lut, last, e & 0x7FFFu, w32);
     const uint32_t len = (le >> 8) ? (le >> 8) : 63u;  // 63: unreachable once phase 1 passed
     return (1u << 30) | (len << 24) | (le & 0xFFu);
 }
@@ -155,13 +169,14 @@ struct Windows {
 template <int C>
 __device__ __forceinline__ void count_codes(const Windows<C> &W, const uint32_t (&gap)[C],
                                             const uint32_t (&lim)[C], const uint8_t *fast,
-                                            const uint16_t *lut, uint32_t n_luts,
+                                            const uint16_t *lut, uint32_t last,
                                             uint32_t (&cnt)[C]) {
-    uint32_t q[C];
+    uint32_t q[C], bad[C];
 #pragma unroll
     for (int c = 0; c < C; c++) {
         q[c] = ~gap[c];
         cnt[c] = 0;
+        bad[c] = 0;
     }
 #pragma unroll
     for (int s = 0; s < 2; s++) {
@@ -170,56 +185,57 @@ __device__ __forceinline__ void count_codes(const Windows<C> &W, const uint32_t 
         for (int c = 0; c < C; c++) qend[c] = ~min(32u * (s + 1), lim[c]);  // p < end <=> q > ~end
         for (;;) {
             bool act[C];
-            uint64_t any = 0;
+            uint64_t am[C], any = 0;
 #pragma unroll
             for (int c = 0; c < C; c++) {
                 act[c] = q[c] > qend[c];
-                any |= ballot(act[c]);
+                am[c] = ballot(act[c]);
+                any |= am[c];
             }
             if (!any) break;
-            uint32_t w32[C], adv[C], m[C];
+            uint32_t w32[C], e[C];
             uint64_t longc = 0;
 #pragma unroll
             for (int c = 0; c < C; c++) {
                 w32[c] = W.at(c, s, q[c]);
-                const uint32_t e = *reinterpret_cast<const uint16_t *>(
+                e[c] = *reinterpret_cast<const uint16_t *>(
                     fast + kCountOff + ((w32[c] >> (32 - DF11_COUNT_BITS)) << 1));
-                // only starts before lim count (lim - p == lim + 1 + q); an inactive
-                // chain counts nothing and does not move
-                const uint32_t cut = min(lim[c] + 1 + q[c], uint32_t(DF11_COUNT_BITS));
-                m[c] = __builtin_amdgcn_ubfe(e, 0, act[c] ? cut : 0u);
-                adv[c] = e >> 12;
-                longc |= ballot(adv[c] == 0);  // inactive lanes only cost a rare detour
+                longc |= ballot(e[c] < (1u << 12)) & am[c];
             }
             if (longc) {  // rare: a first code longer than the count index
 #pragma unroll
                 for (int c = 0; c < C; c++) {
-                    const uint32_t len = walk_tables(lut, n_luts, w32[c]) >> 8;
-                    const bool here = act[c] && adv[c] == 0;
-                    cnt[c] += (here && len == 0) ? kBadCount : 0u;  // no code: corrupt input
-                    m[c] = here ? 1u : m[c];
-                    adv[c] = here ? (len ? len : 64u) : adv[c];
+                    if (act[c] && (e[c] >> 12) == 0) {
+                        const uint32_t len = walk_tables(lut, last, e[c] & 0xFFFu, w32[c]) >> 8;
+                        // one code of that length; none at all means a corrupt input
+                        e[c] = len ? (len << 12) | 1u : (64u << 12);
+                        bad[c] |= len ? 0u : kBadCount;
+                    }
                 }
             }
+            // finished chains are masked off: they count nothing and do not move
 #pragma unroll
             for (int c = 0; c < C; c++) {
-                cnt[c] += uint32_t(__builtin_popcount(m[c]));
-                q[c] -= act[c] ? adv[c] : 0u;
+                if (act[c]) {
+                    // only starts before lim count (lim - p == lim + 1 + q)
+                    const uint32_t cut = min(lim[c] + 1 + q[c], uint32_t(DF11_COUNT_BITS));
+                    cnt[c] += uint32_t(__builtin_popcount(__builtin_amdgcn_ubfe(e[c], 0, cut)));
+                    q[c] -= e[c] >> 12;
+                }
             }
         }
     }
+#pragma unroll
+    for (int c = 0; c < C; c++) cnt[c] += bad[c];
 }
 
-// Phase 2: exponents of window c's codes to stage[dst[c] ..), up to 2 bytes
-// beyond.  Positions are byte offsets into the LDS array, not pointers: a
-// select between pointers held in registers loses the address space and
-// turns the stores into flat (vector memory) stores.
+// Phase 2: exponents of window c's codes to LDS bytes dst[c] .., up to 2
+// bytes beyond.  dst are LDS addresses, so the stores need no base added.
 template <int C>
 __device__ __forceinline__ void decode_codes(const Windows<C> &W, const uint32_t (&gap)[C],
                                              const uint32_t (&lim)[C], const uint8_t *fast,
-                                             const uint16_t *lut, uint32_t n_luts,
-                                             uint8_t *stage, uint32_t (&dst)[C],
-                                             uint32_t trash) {
+                                             const uint16_t *lut, uint32_t last,
+                                             uint32_t (&dst)[C]) {
     uint32_t q[C];
 #pragma unroll
     for (int c = 0; c < C; c++) q[c] = ~gap[c];
@@ -230,11 +246,12 @@ __device__ __forceinline__ void decode_codes(const Windows<C> &W, const uint32_t
         for (int c = 0; c < C; c++) qend[c] = ~min(32u * (s + 1), lim[c]);
         for (;;) {
             bool act[C];
-            uint64_t any = 0;
+            uint64_t am[C], any = 0;
 #pragma unroll
             for (int c = 0; c < C; c++) {
                 act[c] = q[c] > qend[c];
-                any |= ballot(act[c]);
+                am[c] = ballot(act[c]);
+                any |= am[c];
             }
             if (!any) break;
             uint32_t w32[C], e[C];
@@ -244,24 +261,26 @@ __device__ __forceinline__ void decode_codes(const Windows<C> &W, const uint32_t
                 w32[c] = W.at(c, s, q[c]);
                 e[c] = *reinterpret_cast<const uint32_t *>(
                     fast + kMultiOff + ((w32[c] >> (32 - DF11_MULTI_BITS)) << 2));
-                longc |= ballot(e[c] < (1u << 30));  // inactive lanes only cost a rare detour
+                longc |= ballot(e[c] < (1u << 30)) & am[c];
             }
             if (longc) {  // rare: a first code longer than 10 bits
 #pragma unroll
                 for (int c = 0; c < C; c++) {
-                    const uint32_t le = long_entry(lut, n_luts, w32[c]);
-                    e[c] = (e[c] < (1u << 30)) ? le : e[c];
+                    const uint32_t le = long_entry(lut, last, e[c], w32[c]);
+                    e[c] = e[c] < (1u << 30) ? le : e[c];
                 }
             }
+            // finished chains are masked off: they neither write nor move
 #pragma unroll
             for (int c = 0; c < C; c++) {
-                const uint32_t o = act[c] ? dst[c] : trash;
-                stage[o] = uint8_t(e[c]);
-                stage[o + 1] = uint8_t(e[c] >> 8);
-                stage[o + 2] = uint8_t(e[c] >> 16);
-                const uint32_t ea = act[c] ? e[c] : 0u;  // an inactive chain does not move
-                dst[c] += ea >> 30;
-                q[c] -= (ea >> 24) & 0x3Fu;
+                if (act[c]) {
+                    lds8 *o = (lds8 *)size_t(dst[c]);
+                    o[0] = uint8_t(e[c]);
+                    o[1] = uint8_t(e[c] >> 8);
+                    o[2] = uint8_t(e[c] >> 16);
+                    dst[c] += e[c] >> 30;
+                    q[c] -= (e[c] >> 24) & 0x3Fu;
+                }
             }
         }
     }
@@ -271,11 +290,11 @@ __device__ __forceinline__ void decode_codes(const Windows<C> &W, const uint32_t
 template <int C>
 __device__ __forceinline__ uint32_t entry_at(const Windows<C> &W, int c, uint32_t p,
                                              const uint8_t *fast, const uint16_t *lut,
-                                             uint32_t n_luts) {
+                                             uint32_t last) {
     const uint32_t w32 = W.at_low(c, p);
     const uint32_t e = *reinterpret_cast<const uint32_t *>(
         fast + kMultiOff + ((w32 >> (32 - DF11_MULTI_BITS)) << 2));
-    return e < (1u << 30) ? long_entry(lut, n_luts, w32) : e;
+    return e < (1u << 30) ? long_entry(lut, last, e, w32) : e;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -333,7 +352,8 @@ template <int C, int JP>
 __global__ __launch_bounds__(kThreads) void df11_decode(KArgs a) {
     // The fixed-size fast tables are the kernel's only static LDS, at address
     // 0, so their offsets fold into the LDS instructions' immediate offsets.
-    // Dynamic LDS: hierarchical tables, 16 bytes of wave totals, staging, trash.
+    // Dynamic LDS: hierarchical tables 1 .. n_luts - 1 (the root is never
+    // read: the fast tables point past it), 16 bytes of wave totals, staging.
     __shared__ __align__(16) uint8_t fast[kLutOff];
     extern __shared__ __align__(16) uint8_t dyn[];
     constexpr uint32_t W = kThreads * C;  // windows per tile
@@ -342,15 +362,14 @@ __global__ __launch_bounds__(kThreads) void df11_decode(KArgs a) {
 
     TileIn<C> cur;
     cur.load(a, a.tile0 + blockIdx.x, t);
-    for (uint32_t i = 16 * t; i < a.table_bytes; i += 16 * kThreads) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(a.tables + i);
+    for (uint32_t i = 16 * t; i < a.lds_tables; i += 16 * kThreads) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(a.tables + (i < kLutOff ? i : i + 512));
         *reinterpret_cast<uint4 *>(i < kLutOff ? fast + i : dyn + (i - kLutOff)) = v;
     }
     __syncthreads();
     const uint16_t *lut = reinterpret_cast<const uint16_t *>(dyn);
     uint32_t *wave_sum = reinterpret_cast<uint32_t *>(dyn + a.ebuf_off - 16);
     uint8_t *ebuf = dyn + a.ebuf_off;
-    const uint32_t trash = a.exp_cap + 4 * t;  // offsets below are relative to ebuf
 
     for (uint32_t it = blockIdx.x; it < a.n_tiles; it += gridDim.x) {
         const uint32_t tile = a.tile0 + it;
@@ -385,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void df11_decode(KArgs a) {
 
         // phase 1 and the block scan
         uint32_t cnt[C];
-        count_codes<C>(win, gap, lim, fast, lut, a.n_luts, cnt);
+        count_codes<C>(win, gap, lim, fast, lut, a.lut_last, cnt);
         uint32_t mine_total = 0;
 #pragma unroll
         for (int c = 0; c < C; c++) mine_total += cnt[c];
@@ -403,26 +422,28 @@ __global__ __launch_bounds__(kThreads) void df11_decode(KArgs a) {
             continue;
         }
 
-        // phase 2, then repair the two bytes a neighbour's last step may have spilled onto
+        // phase 2, then repair the two bytes a neighbour's last step may have spilled onto;
+        // positions are LDS addresses
         uint32_t first[C], dst[C];
-        first[0] = (P0 - A0) + before + incl - mine_total;
+        first[0] = lds_addr(ebuf) + (P0 - A0) + before + incl - mine_total;
 #pragma unroll
         for (int c = 1; c < C; c++) first[c] = first[c - 1] + cnt[c - 1];
 #pragma unroll
         for (int c = 0; c < C; c++) dst[c] = first[c];
-        decode_codes<C>(win, gap, lim, fast, lut, a.n_luts, ebuf, dst, trash);
+        decode_codes<C>(win, gap, lim, fast, lut, a.lut_last, dst);
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < C; c++) {
             if (cnt[c]) {
-                uint32_t e = entry_at<C>(win, c, gap[c], fast, lut, a.n_luts);
-                ebuf[first[c]] = uint8_t(e);
+                uint32_t e = entry_at<C>(win, c, gap[c], fast, lut, a.lut_last);
+                lds8 *o = (lds8 *)size_t(first[c]);
+                o[0] = uint8_t(e);
                 if (cnt[c] > 1) {
                     if ((e >> 30) < 2)
-                        e = entry_at<C>(win, c, gap[c] + ((e >> 24) & 0x3Fu), fast, lut, a.n_luts);
+                        e = entry_at<C>(win, c, gap[c] + ((e >> 24) & 0x3Fu), fast, lut, a.lut_last);
                     else
                         e >>= 8;
-                    ebuf[first[c] + 1] = uint8_t(e);
+                    o[1] = uint8_t(e);
                 }
             }
         }
@@ -473,10 +494,12 @@ int prepare(const df11_device_stream *s, KArgs &a) {
     a.tables = static_cast<const uint8_t *>(s->tables);
     a.total_bits = s->total_bits;
     a.n_weights = uint32_t(s->n_weights);
-    a.n_luts = s->n_luts;
-    a.table_bytes = kLutOff + 512u * s->n_luts;
-    // dynamic LDS: hierarchical tables, 16 bytes of wave totals, staging, trash
-    a.ebuf_off = 512u * s->n_luts + 16;
+    // LDS holds tables 1 .. n_luts - 1; room for one is kept when there are
+    // none, so that a walk on corrupt input still reads inside the allocation
+    a.lut_last = s->n_luts > 1 ? s->n_luts - 1 : 1u;
+    a.lds_tables = kLutOff + 512u * (s->n_luts - 1);
+    // dynamic LDS: hierarchical tables, 16 bytes of wave totals, staging
+    a.ebuf_off = 512u * a.lut_last + 16;
     // outputs from P0 & ~7 to the last 8-chunk, plus the 2 spill bytes
     a.exp_cap = (s->max_tile_symbols + 7 + 16 + 15) & ~15u;
     return DF11_OK;
@@ -485,7 +508,7 @@ int prepare(const df11_device_stream *s, KArgs &a) {
 int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t st) {
     if (n_tiles == 0) return DF11_OK;
     a.n_tiles = n_tiles;
-    const size_t lds = size_t(a.ebuf_off) + a.exp_cap + 4 * kThreads;
+    const size_t lds = size_t(a.ebuf_off) + a.exp_cap;
     const void *fn = kernel_for(s->tile_windows);
     if (lds > 65536 &&
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)

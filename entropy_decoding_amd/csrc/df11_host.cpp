@@ -246,6 +246,12 @@ void head_code(const df11_codebook *cb, uint32_t v, uint32_t &len, uint32_t &sym
     sym = e & 0xFF;
 }
 
+// The table a root entry points at, or 0 when the entry is a leaf.
+uint32_t level1_table(const df11_codebook *cb, uint32_t top8) {
+    const uint32_t e = cb->lut[0][top8];
+    return (e & 0x8000) ? (e & 0x7FFF) : 0u;
+}
+
 // Multi-code tables for the decoder's fast path.  Bits beyond the index are
 // taken as zero: a code that fits in the remaining index bits is decoded the
 // same whatever follows, and one that does not fit comes out longer than
@@ -263,7 +269,9 @@ void build_multi_tables(df11_codebook *cb) {
             n++;
             used += len;
         }
-        cb->multi[x] = n ? (n << 30) | (used << 24) | syms : 0;
+        // no code fits: the first is longer than 8 bits, so the root entry of
+        // the index's top 8 bits points at the level-1 table to walk from
+        cb->multi[x] = n ? (n << 30) | (used << 24) | syms : level1_table(cb, x >> (kM - 8));
     }
     for (uint32_t x = 0; x < (1u << kC); x++) {
         const uint32_t v = x << (32 - kC);
@@ -275,7 +283,7 @@ void build_multi_tables(df11_codebook *cb) {
             mask |= 1u << used;
             used += len;
         }
-        cb->count[x] = uint16_t(used ? (used << 12) | mask : 0);
+        cb->count[x] = uint16_t(used ? (used << 12) | mask : level1_table(cb, x >> (kC - 8)));
     }
 }
 

@@ -79,13 +79,19 @@ typedef void *df11_hip_stream;
  *                  leaf     bit 15 = 0, bits 13..8 = code length (1..32), bits 7..0 = symbol
  *                  pointer  bit 15 = 1, bits 14..0 = index of the next-level table
  *   multi[1024]  10-bit index; the first up-to-3 codes that lie wholly inside
- *                the 10 bits: bits 31..30 = how many (0 when the first code is
- *                longer than 10 bits), bits 29..24 = their total length, bits
- *                7..0, 15..8, 23..16 = their symbols in order (unused slots 0).
+ *                the 10 bits: bits 31..30 = how many, bits 29..24 = their
+ *                total length, bits 7..0, 15..8, 23..16 = their symbols in
+ *                order (unused slots 0).  When the first code is longer than
+ *                10 bits, bits 31..30 are 0 and the entry is the index of the
+ *                level-1 table that lut[0] points at for the index's top 8 bits.
  *   count[4096]  12-bit index; every code that lies wholly inside the 12 bits:
- *                bits 15..12 = their total length (0 when the first code is
- *                longer than 12 bits), bit j (j < 12) set iff one of them starts
- *                j bits after the index's first bit.
+ *                bits 15..12 = their total length, bit j (j < 12) set iff one
+ *                of them starts j bits after the index's first bit.  When the
+ *                first code is longer than 12 bits, bits 15..12 are 0 and bits
+ *                11..0 hold that level-1 table index.
+ *
+ * The decoder reads lut[0] only through these level-1 indices, so it keeps
+ * lut[1 ..] in on-chip memory and not the root.
  *
  * multi, count and lut[0 .. n_luts) are contiguous: the device copy of the
  * tables is the df11_table_bytes(cb) bytes starting at &cb->multi[0].

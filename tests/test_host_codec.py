@@ -211,11 +211,20 @@ def test_fast_tables_match_a_brute_force_decode(which, unit_tensors):
     table = {(int(l), format(int(codes[s]), f"0{int(l)}b")): s for s, l in enumerate(lens) if l}
     multi = np.ctypeslib.as_array(cb.multi)
     count = np.ctypeslib.as_array(cb.count)
+    root = np.ctypeslib.as_array(cb.lut)[0]
     kM, kC = ed.DF11_MULTI_BITS, ed.DF11_COUNT_BITS
+    n_long = 0
     for x in range(1 << kM):
         got = _greedy_codes(format(x, f"0{kM}b"), table)[:3]
         e = int(multi[x])
         assert e >> 30 == len(got), x
+        if not got:
+            # first code longer than the index: the entry names the level-1
+            # table that the root entry for the top 8 bits points at
+            r = int(root[x >> (kM - 8)])
+            assert r & 0x8000 and e == r & 0x7FFF and e >= 1, x
+            n_long += 1
+            continue
         assert (e >> 24) & 0x3F == sum(l for _, l, _ in got), x
         for i, (_, _, s) in enumerate(got):
             assert (e >> (8 * i)) & 0xFF == s, x
@@ -225,4 +234,9 @@ def test_fast_tables_match_a_brute_force_decode(which, unit_tensors):
         got = _greedy_codes(format(x, f"0{kC}b"), table)
         e = int(count[x])
         assert e >> 12 == sum(l for _, l, _ in got), x
+        if not got:
+            r = int(root[x >> (kC - 8)])
+            assert r & 0x8000 and e == r & 0x7FFF and e >= 1, x
+            continue
         assert e & 0xFFF == sum(1 << pos for pos, _, _ in got), x
+    assert (n_long > 0) == (int(lens.max()) > kM)
