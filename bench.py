@@ -9,7 +9,7 @@ written, whole job over K steps), plus the dominant kernel's HBM roofline
 fraction from algorithmic bytes (compressed arrays read once + BF16 written)
 and the CPU oracle's bit-serial decode timed on this host as a baseline.
 
-  python bench.py [--steps K] [--warmup W] [--config 2|1|0|3a|3b|3c|4] [--tile-windows 256|512]
+  python bench.py [--steps K] [--warmup W] [--config 2|1|0|3a|3b|3c|4] [--tile-windows 64|256|512]
 """
 
 from __future__ import annotations
@@ -128,8 +128,12 @@ def run_unit(name, tensors, args, torch, ed):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     alg = algorithmic_bytes(hs, cb)
-    small = alg < (1 << 30)  # fits the 256 MB last-level cache several times over: flush
-    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev) if small else None
+    # a unit under 1 GiB could be served partly from the 256 MB last-level
+    # cache on the next step: evict it between steps by READING 1 GiB (a
+    # write would leave dirty lines for the timed kernel to write back)
+    small = alg < (1 << 30)
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if small else None
+    sink = torch.zeros((), dtype=torch.int32, device=dev)
 
     for _ in range(args.warmup):
         ed.df11_decompress_block(ds, out, status, stream)
@@ -141,7 +145,7 @@ def run_unit(name, tensors, args, torch, ed):
     t0 = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
-            flush.zero_()
+            torch.amax(flush, dim=0, out=sink)
         starts[i].record(stream)
         ed.df11_decompress_block(ds, out, status, stream)
         ends[i].record(stream)
@@ -169,7 +173,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="2")
-    ap.add_argument("--tile-windows", type=int, default=256, choices=(256, 512))
+    ap.add_argument("--tile-windows", type=int, default=64, choices=(64, 256, 512))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes instead "

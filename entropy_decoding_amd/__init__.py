@@ -36,7 +36,7 @@ DF11_E_CAPACITY = 4
 DF11_E_HIP = 5
 DF11_E_CORRUPT = 6
 
-DEFAULT_TILE_WINDOWS = 256
+DEFAULT_TILE_WINDOWS = 64
 DEFAULT_WINDOW_BYTES = 8
 
 

@@ -287,7 +287,7 @@ void build_multi_tables(df11_codebook *cb) {
     }
 }
 
-bool valid_layout(uint32_t T, uint32_t B) { return B == 8 && (T == 256 || T == 512); }
+bool valid_layout(uint32_t T, uint32_t B) { return B == 8 && (T == 64 || T == 256 || T == 512); }
 
 int log2u(uint64_t x) {
     int r = 0;

@@ -23,8 +23,10 @@
  *                 decompressed by one launch (a tensor, or all weight tensors
  *                 of one transformer block, concatenated in order)
  *   window        B = 8 consecutive stream bytes, decoded serially from its gap
- *   tile          T consecutive windows decoded by one workgroup of 256 threads,
- *                 T / 256 adjacent windows per thread
+ *   tile          T consecutive windows whose outputs are placed by one
+ *                 block_out_pos entry: T = 64 is one wave64 per tile (the
+ *                 default), T = 256 one workgroup of 256 threads, T = 512 one
+ *                 workgroup with two adjacent windows per thread
  *
  * Stream format.  Codes are canonical (symbols ordered by (length, value)
  * take consecutive codes), at most 32 bits long, and written MSB-first: bit j
@@ -190,7 +192,7 @@ int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel,
 /*
  * df11_encode_size -- host.  Sizes of all arrays df11_encode will write for
  * these tensors under layout (tile_windows T, window_bytes B).  Supported
- * layouts: B = 8 with T = 256 or 512.  Errors: DF11_E_INVALID, DF11_E_SYMBOL.
+ * layouts: B = 8 with T = 64, 256 or 512.  Errors: DF11_E_INVALID, DF11_E_SYMBOL.
  */
 int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors,
                      const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,

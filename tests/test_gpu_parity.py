@@ -108,7 +108,7 @@ def check_sampled_tiles(u, out, n_samples=24, seed=0):
 # ------------------------------------------------------------------ small, exhaustive
 
 
-@pytest.mark.parametrize("tw", [256, 512])
+@pytest.mark.parametrize("tw", [64, 256, 512])
 def test_config0_every_output_equals_the_oracle(tw, unit_tensors):
     (w,) = unit_tensors("0")
     ocb = oracle.codebook(w)
@@ -135,7 +135,7 @@ def test_random_multi_tensor_units(seed):
         tensors.append(z.astype(np.uint16))
     if sum(t.size for t in tensors) == 0:
         tensors.append(np.array([0x3F80], dtype=np.uint16))
-    u = Unit(tensors, 512 if seed % 3 else 256)
+    u = Unit(tensors, (64, 256, 512)[seed % 3])
     out = check_identity(u, f"random seed={seed}")
     check_sampled_tiles(u, out, 8, seed)
     offs = u.hs.tensor_offsets
@@ -272,16 +272,16 @@ def test_stress_config_full_size(cfg, unit_tensors):
     check_sampled_tiles(u, out)
 
 
-@pytest.mark.parametrize("cfg", ["1", "2"])
-def test_block_config_full_size(cfg):
+@pytest.mark.parametrize("cfg,tw", [("1", 64), ("1", 256), ("2", 64)])
+def test_block_config_full_size(cfg, tw):
     unit = sw.config(cfg).units[0]
     tensors = sw.gen_unit(unit)
-    u = Unit(tensors)
-    out = check_identity(u, f"cfg{cfg} block", poisons=(-1,))
+    u = Unit(tensors, tw)
+    out = check_identity(u, f"cfg{cfg} block T={tw}", poisons=(-1,))
     check_sampled_tiles(u, out, 16)
     del out
     for k in (0, 6):
-        got, st = u.decompress_tensor(k, 0, f"cfg{cfg}")
+        got, st = u.decompress_tensor(k, 0, f"cfg{cfg} T={tw}")
         assert st == 0 and torch.equal(got, _dev_i16(tensors[k]))
 
 

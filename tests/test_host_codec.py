@@ -64,8 +64,9 @@ def test_stress_configs_match_oracle(unit_tensors, cfg):
     _compare([w[: 1 << 22]])
 
 
-def test_256_window_tiles_match_oracle(unit_tensors):
-    _compare(unit_tensors("0"), threads=256)
+@pytest.mark.parametrize("tw", [64, 256])
+def test_smaller_tiles_match_oracle(unit_tensors, tw):
+    _compare(unit_tensors("0"), threads=tw)
 
 
 def test_multi_tensor_unit_with_ragged_and_empty_tensors():
