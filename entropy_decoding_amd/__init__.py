@@ -112,6 +112,20 @@ class df11_device_stream(ctypes.Structure):
     ]
 
 
+class df11_gemv_tensor(ctypes.Structure):
+    _fields_ = [
+        ("w_offset", ctypes.c_uint64),
+        ("x_offset", ctypes.c_uint64),
+        ("y_offset", ctypes.c_uint64),
+        ("rows", ctypes.c_uint32),
+        ("cols", ctypes.c_uint32),
+    ]
+
+
+DF11_PIPELINE_MAX_SLOTS = 4
+DF11_GEMV_MAX_TENSORS = 16
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run entropy_decoding_amd.build.build_library()")
@@ -134,8 +148,18 @@ def _load():
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.df11_status_string.argtypes = [ctypes.c_int]
     L.df11_status_string.restype = ctypes.c_char_p
+    vp = ctypes.c_void_p
+    L.df11_pipeline_create.argtypes = [vp, ctypes.c_uint32, ctypes.POINTER(vp)]
+    L.df11_pipeline_destroy.argtypes = [vp]
+    L.df11_pipeline_decompress.argtypes = [vp, ctypes.c_uint32, ctypes.POINTER(df11_device_stream),
+                                           vp, vp]
+    L.df11_pipeline_acquire.argtypes = [vp, ctypes.c_uint32, vp]
+    L.df11_pipeline_release.argtypes = [vp, ctypes.c_uint32, vp]
+    L.df11_gemv_bf16.argtypes = [vp, ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32, vp, vp, vp]
     for f in (L.df11_build_codebook, L.df11_encode_size, L.df11_encode,
-              L.df11_decompress_block, L.df11_decompress_tensor):
+              L.df11_decompress_block, L.df11_decompress_tensor, L.df11_pipeline_create,
+              L.df11_pipeline_destroy, L.df11_pipeline_decompress, L.df11_pipeline_acquire,
+              L.df11_pipeline_release, L.df11_gemv_bf16):
         f.restype = ctypes.c_int
     return L
 
@@ -334,6 +358,76 @@ def df11_decompress_tensor(ds: DeviceStream, k: int, out, status=None, stream=No
            LIB.df11_decompress_tensor(ctypes.byref(ds.desc), int(k),
                                       ctypes.c_void_p(out.data_ptr()), sp,
                                       _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------- block pipeline
+
+
+class Pipeline:
+    """df11_pipeline_*: a ring of n_slots output buffers decompressed on
+    ``decode_stream`` and read by consumer streams, ordered by events."""
+
+    def __init__(self, decode_stream, n_slots: int = 2):
+        self._p = ctypes.c_void_p(0)
+        self.decode_stream = decode_stream
+        _check("df11_pipeline_create",
+               LIB.df11_pipeline_create(_stream_handle(decode_stream), int(n_slots),
+                                        ctypes.byref(self._p)))
+
+    def decompress(self, slot: int, ds: DeviceStream, out, status=None) -> None:
+        if out.numel() < ds.n_weights or out.element_size() != 2 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous 16-bit device tensor of n_weights elements")
+        sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
+        _check("df11_pipeline_decompress",
+               LIB.df11_pipeline_decompress(self._p, int(slot), ctypes.byref(ds.desc),
+                                            ctypes.c_void_p(out.data_ptr()), sp))
+
+    def acquire(self, slot: int, consumer_stream) -> None:
+        _check("df11_pipeline_acquire",
+               LIB.df11_pipeline_acquire(self._p, int(slot), _stream_handle(consumer_stream)))
+
+    def release(self, slot: int, consumer_stream) -> None:
+        _check("df11_pipeline_release",
+               LIB.df11_pipeline_release(self._p, int(slot), _stream_handle(consumer_stream)))
+
+    def close(self) -> None:
+        if self._p:
+            _check("df11_pipeline_destroy", LIB.df11_pipeline_destroy(self._p))
+            self._p = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gemv_layout(shapes):
+    """df11_gemv_tensor descriptors for row-major matrices stored back to back
+    (one decompressed unit), with x and y slices also back to back."""
+    descs, w, x, y = [], 0, 0, 0
+    for rows, cols in shapes:
+        descs.append((w, x, y, rows, cols))
+        w += rows * cols
+        x += cols
+        y += rows
+    arr = (df11_gemv_tensor * max(len(descs), 1))()
+    for i, (wo, xo, yo, r, c) in enumerate(descs):
+        arr[i].w_offset, arr[i].x_offset, arr[i].y_offset, arr[i].rows, arr[i].cols = wo, xo, yo, r, c
+    return arr, len(descs), x, y
+
+
+def df11_gemv_bf16(w, layout, x, y, stream=None) -> None:
+    """y = W x per tensor of ``layout`` (from gemv_layout) over the 16-bit
+    device tensor ``w``; x and y are float32 device tensors."""
+    arr, n, nx, ny = layout
+    if w.element_size() != 2 or x.dtype.itemsize != 4 or y.dtype.itemsize != 4:
+        raise ValueError("w must be 16-bit, x and y float32")
+    if x.numel() < nx or y.numel() < ny:
+        raise ValueError("x or y too small for the layout")
+    _check("df11_gemv_bf16",
+           LIB.df11_gemv_bf16(ctypes.c_void_p(w.data_ptr()), arr, n, ctypes.c_void_p(x.data_ptr()),
+                              ctypes.c_void_p(y.data_ptr()), _stream_handle(stream)))
 
 
 def table_bytes(cb: df11_codebook) -> int:

@@ -239,6 +239,76 @@ int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, uint16_t *ou
 /* Static description of a status code. */
 const char *df11_status_string(int status);
 
+/*
+ * Overlapped block pipeline -- device orchestration.  Decompression is done
+ * per transformer block so that the next block's weights can be prepared
+ * while the model consumes the current one ("transformer-block-level
+ * decompression", DFloat11 abstract).  A df11_pipeline owns no device memory:
+ * it keeps, for each of n_slots caller-owned output buffers, one event that
+ * marks "decompressed into this slot" and one that marks "the consumer has
+ * finished reading it", and orders a decode stream against consumer streams
+ * with them.  Typical use with two slots:
+ *
+ *   decompress(slot 0, block 0)
+ *   for i: decompress(slot (i+1)%2, block i+1)   -- decode stream, waits for the
+ *                                                   release of that slot
+ *          acquire(slot i%2, compute stream)     -- compute waits for block i
+ *          ... consumer kernels on compute reading slot i%2 ...
+ *          release(slot i%2, compute stream)
+ *
+ * All calls only enqueue work or waits and return at once.  A pipeline is
+ * used from one host thread at a time; its streams must outlive it.
+ */
+#define DF11_PIPELINE_MAX_SLOTS 4
+typedef struct df11_pipeline df11_pipeline;  /* opaque */
+
+/* Creates a pipeline over n_slots (1..DF11_PIPELINE_MAX_SLOTS) buffers whose
+ * decompressions run on decode_stream (2 * n_slots HIP events are created).
+ * Errors: DF11_E_INVALID, DF11_E_HIP.  *out is null on error. */
+int df11_pipeline_create(df11_hip_stream decode_stream, uint32_t n_slots, df11_pipeline **out);
+
+/* Destroys the events and the object; null is allowed.  Work already enqueued
+ * is not waited for. */
+int df11_pipeline_destroy(df11_pipeline *p);
+
+/* Enqueues on the decode stream: a wait for the slot's last release (if it
+ * was ever released), df11_decompress_block(s, out, d_status), and the slot's
+ * ready event.  Same argument errors as df11_decompress_block.  A slot that a
+ * consumer has read must be released before it is refilled. */
+int df11_pipeline_decompress(df11_pipeline *p, uint32_t slot, const df11_device_stream *s,
+                             uint16_t *out, int32_t *d_status);
+
+/* Makes the consumer stream wait until the slot's latest decompression is
+ * done.  DF11_E_INVALID if the slot was never filled. */
+int df11_pipeline_acquire(df11_pipeline *p, uint32_t slot, df11_hip_stream consumer);
+
+/* Records, on the consumer stream, that the work enqueued there so far is all
+ * that reads the slot; the next decompression into it waits for that work. */
+int df11_pipeline_release(df11_pipeline *p, uint32_t slot, df11_hip_stream consumer);
+
+/*
+ * df11_gemv_bf16 -- device, a consumer of decompressed blocks: for each of
+ * n_tensors (<= DF11_GEMV_MAX_TENSORS) row-major BF16 matrices
+ * W_k = w[w_offset_k ..] of rows_k x cols_k, y[y_offset_k + r] = sum over c of
+ * W_k[r][c] * x[x_offset_k + c], in float32 (products and sums are fused
+ * multiply-adds in a fixed order: 8-column groups per lane in column order,
+ * then a butterfly over the 64 lanes, so results are deterministic).  One
+ * launch on stream st.  Requirements: w and x 16-byte aligned, cols_k and
+ * w_offset_k multiples of 8, x_offset_k a multiple of 4 (DF11_E_INVALID).
+ * Offsets are in elements.
+ */
+#define DF11_GEMV_MAX_TENSORS 16
+typedef struct df11_gemv_tensor {
+    uint64_t w_offset;
+    uint64_t x_offset;
+    uint64_t y_offset;
+    uint32_t rows;
+    uint32_t cols;
+} df11_gemv_tensor;
+
+int df11_gemv_bf16(const uint16_t *w, const df11_gemv_tensor *tensors, uint32_t n_tensors,
+                   const float *x, float *y, df11_hip_stream st);
+
 #ifdef __cplusplus
 }
 #endif

@@ -270,3 +270,31 @@ def gaussian_exponent_probs(sigma: float) -> np.ndarray:
         lo, hi = 2.0 ** (e - 127), 2.0 ** (e - 126)
         p[e] = 2.0 * (phi(hi / sigma) - phi(lo / sigma))
     return p
+
+
+# ---------------------------------------------------------------- GEMV consumer
+
+
+def bf16_to_f64(w: np.ndarray) -> np.ndarray:
+    """Exact values of BF16 bit patterns: the pattern is the top half of an fp32."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    return (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def gemv(w_flat: np.ndarray, shapes, x_flat: np.ndarray) -> np.ndarray:
+    """y = W_k x_k for row-major BF16 matrices stored back to back in w_flat
+    (shapes: (rows, cols) each), x slices back to back in x_flat; float64.
+
+    Products of a BF16 and an fp32 value are exact in float64, and a row of at
+    most 2^20 terms sums with relative error below 2^-32, far inside any fp32
+    tolerance.
+    """
+    w = bf16_to_f64(np.asarray(w_flat).reshape(-1))
+    x = np.asarray(x_flat, dtype=np.float64).reshape(-1)
+    ys, wo, xo = [], 0, 0
+    for rows, cols in shapes:
+        W = w[wo:wo + rows * cols].reshape(rows, cols)
+        ys.append(W @ x[xo:xo + cols])
+        wo += rows * cols
+        xo += cols
+    return np.concatenate(ys) if ys else np.zeros(0)

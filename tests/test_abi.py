@@ -49,6 +49,8 @@ int main(void) {{
          sizeof(df11_host_stream), sizeof(df11_device_stream));
   printf("%zu %zu %zu\\n", offsetof(df11_codebook, lut), offsetof(df11_host_stream, n_weights),
          offsetof(df11_device_stream, n_luts));
+  printf("%zu %zu %zu %d %d\\n", sizeof(df11_gemv_tensor), offsetof(df11_gemv_tensor, rows),
+         offsetof(df11_gemv_tensor, cols), DF11_PIPELINE_MAX_SLOTS, DF11_GEMV_MAX_TENSORS);
   return 0;
 }}
 '''
@@ -66,6 +68,10 @@ int main(void) {{
                      ctypes.sizeof(ed.df11_host_stream), ctypes.sizeof(ed.df11_device_stream)]
     assert offs == [ed.df11_codebook.lut.offset, ed.df11_host_stream.n_weights.offset,
                     ed.df11_device_stream.n_luts.offset]
+    g = [int(x) for x in lines[2].split()]
+    assert g == [ctypes.sizeof(ed.df11_gemv_tensor), ed.df11_gemv_tensor.rows.offset,
+                 ed.df11_gemv_tensor.cols.offset, ed.DF11_PIPELINE_MAX_SLOTS,
+                 ed.DF11_GEMV_MAX_TENSORS]
 
 
 def test_status_strings():

@@ -332,3 +332,45 @@ def test_round_trip_stress_configs(unit_tensors):
         (w,) = unit_tensors(cfg)
         w = w[: 1 << 21]
         _round_trip(w)
+
+
+# ------------------------------------------------------------------ GEMV consumer oracle
+
+
+def test_bf16_values_are_exact():
+    pats = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x0001, 0x3E80, 0x4049],
+                    dtype=np.uint16)
+    got = oracle.bf16_to_f64(pats)
+    want = [1.0, -2.0, 0.0, -0.0, np.inf, -np.inf, 2.0 ** -133, 0.25, 3.140625]
+    assert np.array_equal(got, np.array(want)) and np.signbit(got[3])
+
+
+def test_gemv_closed_forms_and_brute_force():
+    # ones: y = cols; identity-like selection: y_r = x_r; then a brute-force loop
+    rows, cols = 5, 24
+    ones = np.full(rows * cols, 0x3F80, dtype=np.uint16)
+    x = np.arange(cols, dtype=np.float32) * 0.5
+    assert np.array_equal(oracle.gemv(ones, [(rows, cols)], x), np.full(rows, x.sum()))
+    sel = np.zeros((rows, cols), dtype=np.uint16)
+    sel[np.arange(rows), np.arange(rows) * 3] = 0x3F80
+    assert np.array_equal(oracle.gemv(sel.reshape(-1), [(rows, cols)], x), x[np.arange(rows) * 3])
+    rng = np.random.default_rng(5)
+    shapes = [(3, 8), (2, 16)]
+    w = (rng.standard_normal(3 * 8 + 2 * 16).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    xs = rng.standard_normal(8 + 16).astype(np.float32)
+    y = oracle.gemv(w, shapes, xs)
+    import struct
+
+    def bf16(v):  # the pattern as the high half of an IEEE single
+        return struct.unpack("<f", struct.pack("<I", int(v) << 16))[0]
+
+    ref, wo, xo = [], 0, 0
+    for r, c in shapes:
+        for i in range(r):
+            acc = 0.0
+            for j in range(c):
+                acc += bf16(w[wo + i * c + j]) * float(xs[xo + j])
+            ref.append(acc)
+        wo += r * c
+        xo += c
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
