@@ -70,6 +70,18 @@ def lib():
             f.restype = ctypes.c_int
         L.oracle_decode.argtypes = [u8p, u64, u64, u8p, u8p, u64, u16p]
         L.oracle_decode.restype = ctypes.c_int
+        L.oracle_fp8_split.argtypes = [u8p, u64, ctypes.c_int, u8p, u8p]
+        L.oracle_fp8_split.restype = ctypes.c_int
+        L.oracle_fp8_merge.argtypes = [u8p, u8p, u64, ctypes.c_int, u8p]
+        L.oracle_fp8_merge.restype = ctypes.c_int
+        L.oracle_histogram_symbols.argtypes = [u8p, u64, u64p]
+        L.oracle_histogram_symbols.restype = None
+        L.oracle_encode_symbols.argtypes = [u8p, u64, u8p, u32p, u8p, u64, u64p]
+        L.oracle_encode_symbols.restype = ctypes.c_int
+        L.oracle_aux_symbols.argtypes = [u8p, u64, u8p, u32, u32, u8p, u64, u32p, u64]
+        L.oracle_aux_symbols.restype = ctypes.c_int
+        L.oracle_decode_symbols.argtypes = [u8p, u64, u64, u8p, u64, u8p]
+        L.oracle_decode_symbols.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -298,3 +310,91 @@ def gemv(w_flat: np.ndarray, shapes, x_flat: np.ndarray) -> np.ndarray:
         wo += rows * cols
         xo += cols
     return np.concatenate(ys) if ys else np.zeros(0)
+
+
+# ---------------------------------------------------------------- FP8 weights
+# (the C file's FP8 section gives the formats and the readings)
+
+FP8_FORMATS = {"e4m3": 1, "e5m2": 2}
+
+
+def fp8_split(b: np.ndarray, fmt: str):
+    """(symbols uint8[n], packed sign+mantissa nibbles uint8[ceil(n/2)])."""
+    b = np.ascontiguousarray(b, dtype=np.uint8).reshape(-1)
+    sym = np.zeros(b.size, dtype=np.uint8)
+    sm = np.zeros((b.size + 1) // 2, dtype=np.uint8)
+    if b.size:
+        r = lib().oracle_fp8_split(_p(b, ctypes.c_uint8), b.size, FP8_FORMATS[fmt],
+                                   _p(sym, ctypes.c_uint8), _p(sm, ctypes.c_uint8))
+        assert r == 0
+    return sym, sm
+
+
+def fp8_merge(sym: np.ndarray, sm: np.ndarray, fmt: str) -> np.ndarray:
+    sym = np.ascontiguousarray(sym, dtype=np.uint8)
+    sm = np.ascontiguousarray(sm, dtype=np.uint8)
+    out = np.zeros(sym.size, dtype=np.uint8)
+    if sym.size:
+        r = lib().oracle_fp8_merge(_p(sym, ctypes.c_uint8), _p(sm, ctypes.c_uint8), sym.size,
+                                   FP8_FORMATS[fmt], _p(out, ctypes.c_uint8))
+        assert r == 0
+    return out
+
+
+def histogram_symbols(sym: np.ndarray) -> np.ndarray:
+    sym = np.ascontiguousarray(sym, dtype=np.uint8).reshape(-1)
+    c = np.zeros(256, dtype=np.uint64)
+    lib().oracle_histogram_symbols(_p(sym, ctypes.c_uint8), sym.size, _p(c, ctypes.c_uint64))
+    return c
+
+
+def codebook_symbols(sym: np.ndarray) -> Codebook:
+    counts = histogram_symbols(sym)
+    lens = code_lengths(counts)
+    return Codebook(counts, lens, canonical_codes(lens))
+
+
+def encode_symbols(sym: np.ndarray, cb: Codebook):
+    """(stream bytes, total_bits) of the symbol sequence."""
+    sym = np.ascontiguousarray(sym, dtype=np.uint8).reshape(-1)
+    lens = np.ascontiguousarray(cb.lens, dtype=np.uint8)
+    codes = np.ascontiguousarray(cb.codes, dtype=np.uint32)
+    total = total_code_bits(histogram_symbols(sym), lens)
+    stream = np.zeros(max(1, (total + 7) // 8), dtype=np.uint8)
+    tb = np.zeros(1, dtype=np.uint64)
+    r = lib().oracle_encode_symbols(_p(sym, ctypes.c_uint8), sym.size, _p(lens, ctypes.c_uint8),
+                                    _p(codes, ctypes.c_uint32), _p(stream, ctypes.c_uint8),
+                                    stream.size, _p(tb, ctypes.c_uint64))
+    if r != 0:
+        raise ValueError(f"oracle_encode_symbols failed ({r})")
+    assert int(tb[0]) == total
+    return stream[: (total + 7) // 8], total
+
+
+def aux_symbols(sym: np.ndarray, cb: Codebook, tile_windows: int, window_bytes: int):
+    sym = np.ascontiguousarray(sym, dtype=np.uint8).reshape(-1)
+    lens = np.ascontiguousarray(cb.lens, dtype=np.uint8)
+    total = total_code_bits(histogram_symbols(sym), lens)
+    window_bits = 8 * window_bytes
+    n_tiles = (total + window_bits * tile_windows - 1) // (window_bits * tile_windows)
+    gaps = np.zeros(n_tiles * tile_windows, dtype=np.uint8)
+    bop = np.zeros(n_tiles + 1, dtype=np.uint32)
+    r = lib().oracle_aux_symbols(_p(sym, ctypes.c_uint8), sym.size, _p(lens, ctypes.c_uint8),
+                                 window_bits, tile_windows, _p(gaps, ctypes.c_uint8), gaps.size,
+                                 _p(bop, ctypes.c_uint32), n_tiles)
+    if r != 0:
+        raise ValueError(f"oracle_aux_symbols failed ({r})")
+    return gaps, bop
+
+
+def decode_symbols(stream: np.ndarray, start_bit: int, end_bit: int, lens, n: int) -> np.ndarray:
+    stream = np.ascontiguousarray(stream, dtype=np.uint8)
+    lens = np.ascontiguousarray(lens, dtype=np.uint8)
+    out = np.zeros(n, dtype=np.uint8)
+    if n == 0:
+        return out
+    r = lib().oracle_decode_symbols(_p(stream, ctypes.c_uint8), start_bit, end_bit,
+                                    _p(lens, ctypes.c_uint8), n, _p(out, ctypes.c_uint8))
+    if r != 0:
+        raise ValueError(f"oracle_decode_symbols failed ({r})")
+    return out

@@ -419,3 +419,166 @@ int oracle_decode(const uint8_t *stream, uint64_t start_bit, uint64_t end_bit,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ FP8 weights
+ *
+ * The same coding applied to 8-bit floating-point weights ("To Compress or
+ * Not? ... Exponent Concentration", abstract: the exponents of FP8 weights are
+ * concentrated too).  Formats (OCP 8-bit floating point):
+ *   fmt 1 = E4M3: bit 7 sign, bits 6..3 exponent, bits 2..0 mantissa;
+ *   fmt 2 = E5M2: bit 7 sign, bits 6..2 exponent, bits 1..0 mantissa.
+ * Readings (the pages give no layout): the symbol is the exponent field; the
+ * sign and mantissa form one 4-bit value, sign just above the mantissa
+ * (E4M3: s<<3 | m; E5M2: s<<2 | m), stored two per byte with the
+ * lower-indexed weight in the low nibble.
+ */
+
+static int fp8_fields(int fmt, int *ebits, int *mbits)
+{
+    if (fmt == 1) { *ebits = 4; *mbits = 3; return 0; }
+    if (fmt == 2) { *ebits = 5; *mbits = 2; return 0; }
+    return -1;
+}
+
+/* sym[i] = exponent field of b[i]; smpack nibble i = sign and mantissa of b[i]. */
+int oracle_fp8_split(const uint8_t *b, uint64_t n, int fmt, uint8_t *sym, uint8_t *smpack)
+{
+    int eb, mb;
+    if (fp8_fields(fmt, &eb, &mb))
+        return -1;
+    memset(smpack, 0, (size_t)((n + 1) / 2));
+    for (uint64_t i = 0; i < n; i++) {
+        unsigned s = b[i] >> 7;
+        unsigned e = (b[i] >> mb) & ((1u << eb) - 1u);
+        unsigned m = b[i] & ((1u << mb) - 1u);
+        unsigned nib = (s << mb) | m;
+        sym[i] = (uint8_t)e;
+        smpack[i / 2] |= (uint8_t)(nib << (4 * (i % 2)));
+    }
+    return 0;
+}
+
+/* The inverse: out[i] = s << 7 | e << mbits | m. */
+int oracle_fp8_merge(const uint8_t *sym, const uint8_t *smpack, uint64_t n, int fmt, uint8_t *out)
+{
+    int eb, mb;
+    if (fp8_fields(fmt, &eb, &mb))
+        return -1;
+    for (uint64_t i = 0; i < n; i++) {
+        unsigned nib = (smpack[i / 2] >> (4 * (i % 2))) & 0xFu;
+        unsigned s = (nib >> mb) & 1u;
+        unsigned m = nib & ((1u << mb) - 1u);
+        out[i] = (uint8_t)((s << 7) | ((unsigned)sym[i] << mb) | m);
+    }
+    return 0;
+}
+
+void oracle_histogram_symbols(const uint8_t *sym, uint64_t n, uint64_t *counts)
+{
+    for (int s = 0; s < NSYM; s++)
+        counts[s] = 0;
+    for (uint64_t i = 0; i < n; i++)
+        counts[sym[i]] += 1;
+}
+
+/* The bit-serial encoder of oracle_encode for a symbol sequence (no sm bytes). */
+int oracle_encode_symbols(const uint8_t *sym, uint64_t n, const uint8_t *lens,
+                          const uint32_t *codes, uint8_t *stream, uint64_t stream_bytes,
+                          uint64_t *total_bits)
+{
+    memset(stream, 0, (size_t)stream_bytes);
+    uint64_t pos = 0;
+    for (uint64_t i = 0; i < n; i++) {
+        int e = sym[i];
+        int l = lens[e];
+        if (l == 0)
+            return -1;
+        if ((pos + (uint64_t)l + 7) / 8 > stream_bytes)
+            return -2;
+        for (int k = l - 1; k >= 0; k--) {
+            if ((codes[e] >> k) & 1u)
+                stream[pos / 8] |= (uint8_t)(0x80u >> (pos % 8));
+            pos++;
+        }
+    }
+    *total_bits = pos;
+    return 0;
+}
+
+/* oracle_aux_fast for a symbol sequence: same definitions of gaps and block_out_pos. */
+int oracle_aux_symbols(const uint8_t *sym, uint64_t n, const uint8_t *lens,
+                       uint32_t window_bits, uint32_t tile_windows,
+                       uint8_t *gaps, uint64_t n_windows, uint32_t *block_out_pos, uint64_t n_tiles)
+{
+    if (window_bits == 0 || tile_windows == 0 || n_windows != n_tiles * tile_windows)
+        return -1;
+    for (uint64_t j = 0; j < n_windows; j++)
+        gaps[j] = 255;
+    uint64_t *starts_in_tile = (uint64_t *)calloc((size_t)n_tiles + 1, sizeof(uint64_t));
+    uint64_t start = 0;
+    uint64_t tile_bits = (uint64_t)window_bits * tile_windows;
+    for (uint64_t i = 0; i < n; i++) {
+        uint64_t j = start / window_bits;
+        if (j >= n_windows) {
+            free(starts_in_tile);
+            return -1;
+        }
+        if (gaps[j] == 255)
+            gaps[j] = (uint8_t)(start - j * window_bits);
+        starts_in_tile[start / tile_bits] += 1;
+        start += lens[sym[i]];
+    }
+    uint64_t acc = 0;
+    for (uint64_t t = 0; t <= n_tiles; t++) {
+        block_out_pos[t] = (uint32_t)acc;
+        if (t < n_tiles)
+            acc += starts_in_tile[t];
+    }
+    free(starts_in_tile);
+    return 0;
+}
+
+/* The textbook decoder of oracle_decode, returning the symbols themselves. */
+int oracle_decode_symbols(const uint8_t *stream, uint64_t start_bit, uint64_t end_bit,
+                          const uint8_t *lens, uint64_t n, uint8_t *sym_out)
+{
+    uint32_t count[MAXLEN + 1], first[MAXLEN + 1], offset[MAXLEN + 1];
+    int sorted[NSYM];
+    int nsorted = 0;
+    for (int l = 0; l <= MAXLEN; l++)
+        count[l] = 0;
+    for (int s = 0; s < NSYM; s++)
+        if (lens[s] >= 1 && lens[s] <= MAXLEN)
+            count[lens[s]] += 1;
+    for (int l = 1; l <= MAXLEN; l++)
+        for (int s = 0; s < NSYM; s++)
+            if (lens[s] == l)
+                sorted[nsorted++] = s;
+    uint64_t code = 0;
+    uint32_t off = 0;
+    for (int l = 1; l <= MAXLEN; l++) {
+        first[l] = (uint32_t)code;
+        offset[l] = off;
+        off += count[l];
+        code = (code + count[l]) << 1;
+    }
+    uint64_t pos = start_bit;
+    for (uint64_t i = 0; i < n; i++) {
+        uint64_t v = 0;
+        int l = 0;
+        int sym = -1;
+        while (sym < 0) {
+            if (pos >= end_bit)
+                return -1;
+            v = (v << 1) | ((stream[pos / 8] >> (7 - pos % 8)) & 1u);
+            pos++;
+            l++;
+            if (l > MAXLEN)
+                return -2;
+            if (count[l] != 0 && v >= first[l] && v - first[l] < count[l])
+                sym = sorted[offset[l] + (uint32_t)(v - first[l])];
+        }
+        sym_out[i] = (uint8_t)sym;
+    }
+    return 0;
+}

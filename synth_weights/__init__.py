@@ -1,4 +1,4 @@
-"""Seeded synthetic BF16 weight generators.
+"""Seeded synthetic BF16 (and FP8) weight generators.
 
 This module produces the uint16 bit patterns that both the CPU oracle and the
 HIP library are fed.  It holds no part of the codec (no histogram, no code
@@ -19,6 +19,9 @@ Recipe (every draw is reproducible from the integers below):
   fill runs on a thread pool (numpy releases the GIL while filling).
 * "lognormal rows": s_r = exp(N(ln 0.02, 0.3^2)) drawn in float64 and cast to
   fp32; w = bf16(s_r * z) with z ~ N(0, 1) in fp32.
+* FP8 variants of a unit: each BF16 tensor scaled so that its largest
+  magnitude maps to the format's largest finite value (448 for E4M3, 57344
+  for E5M2), then rounded to nearest, ties to even, saturating.
 """
 
 from __future__ import annotations
@@ -118,6 +121,53 @@ def bf16_from_f32(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
+
+
+# OCP 8-bit floating point formats: exponent bits, mantissa bits, bias, largest finite value
+FP8_FORMATS = {"e4m3": (4, 3, 7, 448.0), "e5m2": (5, 2, 15, 57344.0)}
+
+
+def fp8_from_f32(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Round fp32 values to an FP8 format (nearest, ties to even, saturating at
+    the largest finite value) and return the uint8 bit patterns.  Computed in
+    float64, where every step below is exact for fp32 inputs."""
+    e_bits, m_bits, bias, max_finite = FP8_FORMATS[fmt]
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    sign = np.signbit(x).astype(np.uint8)
+    a = np.abs(x)
+    emin = 1 - bias  # exponent of the smallest normal
+    _, e = np.frexp(a)  # a = f * 2^e with f in [0.5, 1): floor(log2 a) = e - 1
+    e = np.maximum(e.astype(np.int64) - 1, emin)
+    q = np.ldexp(1.0, e - m_bits)  # spacing of representable values around a
+    r = np.minimum(np.round(a / q) * q, max_finite)  # numpy rounds halves to even
+    _, er = np.frexp(r)
+    er = er.astype(np.int64) - 1
+    normal = r >= np.ldexp(1.0, emin)
+    field = np.where(normal, er + bias, 0)
+    mant = np.where(normal, r / np.ldexp(1.0, np.where(normal, er, 0) - m_bits) - (1 << m_bits),
+                    r / np.ldexp(1.0, emin - m_bits))
+    return ((sign << 7) | (field.astype(np.uint8) << m_bits) | mant.astype(np.uint8)).astype(np.uint8)
+
+
+def gen_unit_fp8(unit: "Unit", fmt: str, threads: int | None = None) -> list:
+    """The unit's tensors quantized to FP8: each BF16 tensor from gen_unit is
+    scaled so its largest magnitude maps to the format's largest finite value
+    (a per-tensor scale, as FP8 checkpoints store one) and rounded."""
+    max_finite = FP8_FORMATS[fmt][3]
+    out = []
+    with ThreadPoolExecutor(_threads(threads)) as pool:
+        for w in gen_unit(unit, threads):
+            v = (w.astype(np.uint32) << np.uint32(16)).view(np.float32)
+            amax = float(np.max(np.abs(v))) if v.size else 0.0
+            scale = np.float32(max_finite / amax) if amax > 0 else np.float32(1.0)
+            q = np.empty(v.size, dtype=np.uint8)
+
+            def conv(lo, v=v, q=q, scale=scale):
+                q[lo:lo + CHUNK_ELEMS] = fp8_from_f32(v[lo:lo + CHUNK_ELEMS] * scale, fmt)
+
+            list(pool.map(conv, range(0, v.size, CHUNK_ELEMS)))
+            out.append(q)
+    return out
 
 
 def _threads(threads: int | None) -> int:

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth_weights as sw
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -374,3 +375,72 @@ def test_gemv_closed_forms_and_brute_force():
         wo += r * c
         xo += c
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ FP8 weights
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_fields_round_trip_every_byte(fmt):
+    b = np.arange(256, dtype=np.uint8)
+    sym, sm = oracle.fp8_split(b, fmt)
+    assert np.array_equal(oracle.fp8_merge(sym, sm, fmt), b)
+    assert sym.max() == (15 if fmt == "e4m3" else 31) and sm.size == 128
+
+
+def test_fp8_field_values_from_the_format_definitions():
+    # E4M3 (bias 7): 1.0 = 0 0111 000, -1.0 = 1 0111 000, 448 = 0 1111 110
+    sym, sm = oracle.fp8_split(np.array([0x38, 0xB8, 0x7E], np.uint8), "e4m3")
+    assert sym.tolist() == [7, 7, 15]
+    assert sm.tolist() == [0x80, 0x06]  # nibbles 0, 8 | 6 (sign above the 3 mantissa bits)
+    # E5M2 (bias 15): 1.0 = 0 01111 00, -57344 = 1 11110 11
+    sym, sm = oracle.fp8_split(np.array([0x3C, 0xFB], np.uint8), "e5m2")
+    assert sym.tolist() == [15, 30] and sm.tolist() == [0x70]  # nibbles 0 and 4|3
+
+
+@pytest.mark.parametrize("fmt,width", [("e4m3", 4), ("e5m2", 5)])
+def test_fp8_uniform_exponents_give_fixed_width_codes(fmt, width):
+    # every exponent equally frequent: all codes have the field's width and the
+    # canonical code of symbol s is s, so the stream is the exponents packed MSB-first
+    rng = np.random.default_rng(3)
+    nsym = 1 << width
+    e = np.repeat(np.arange(nsym, dtype=np.uint8), 40)
+    rng.shuffle(e)
+    b = (e.astype(np.uint16) << (7 - width)).astype(np.uint8) | rng.integers(0, 2, e.size).astype(np.uint8) << 7
+    sym, _ = oracle.fp8_split(b, fmt)
+    cb = oracle.codebook_symbols(sym)
+    assert (cb.lens[:nsym] == width).all() and (cb.lens[nsym:] == 0).all()
+    stream, total = oracle.encode_symbols(sym, cb)
+    bits = "".join(format(int(s), f"0{width}b") for s in e)
+    assert total == len(bits) and len(bits) % 8 == 0
+    assert stream.tobytes() == int(bits, 2).to_bytes(len(bits) // 8, "big")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_quantized_gaussian_round_trips_within_the_entropy_bound(fmt, unit_tensors):
+    (w,) = unit_tensors("0")
+    b = sw.fp8_from_f32((w.astype(np.uint32) << 16).view(np.float32) * np.float32(20000), fmt)
+    sym, sm = oracle.fp8_split(b, fmt)
+    cb = oracle.codebook_symbols(sym)
+    H = oracle.entropy_bits(cb.counts)
+    L = oracle.mean_code_length(cb.counts, cb.lens)
+    assert H <= L < H + 1
+    assert oracle.kraft_numerator(cb.lens) == 1 << 32
+    stream, total = oracle.encode_symbols(sym, cb)
+    dec = oracle.decode_symbols(stream, 0, total, cb.lens, sym.size)
+    assert np.array_equal(oracle.fp8_merge(dec, sm, fmt), b)
+
+
+def test_fp8_aux_arrays_from_their_definition():
+    rng = np.random.default_rng(12)
+    sym = rng.choice(16, size=20000, p=np.r_[[0.3, 0.25, 0.15, 0.1], np.full(12, 0.2 / 12)]).astype(np.uint8)
+    cb = oracle.codebook_symbols(sym)
+    T, B = 8, 8
+    gaps, bop = oracle.aux_symbols(sym, cb, T, B)
+    starts = np.concatenate([[0], np.cumsum(cb.lens[sym].astype(np.int64))[:-1]])
+    wb = 64
+    for j in range(gaps.size):
+        inside = starts[(starts >= j * wb) & (starts < (j + 1) * wb)]
+        assert gaps[j] == (inside[0] - j * wb if inside.size else 255)
+    for t in range(bop.size):
+        assert bop[t] == np.count_nonzero(starts < t * T * wb) or (t == bop.size - 1 and bop[t] == sym.size)
