@@ -44,13 +44,15 @@ def kernel_hash() -> str:
 
 
 def algorithmic_bytes(hs, cb) -> int:
-    """Compressed arrays read once (stream payload, sm, gaps, block_out_pos, tables)
-    plus 2 bytes of BF16 written per weight."""
+    """Compressed arrays read once (stream payload, sign+mantissa array, gaps,
+    block_out_pos, tables) plus the output written: 2 bytes per BF16 weight, 1
+    per FP8 weight."""
     import entropy_decoding_amd as ed
 
-    read = (hs.total_bits + 7) // 8 + hs.n_weights + hs.gaps.size + 4 * hs.block_out_pos.size \
+    sm = hs.n_weights if hs.format == 0 else (hs.n_weights + 1) // 2
+    read = (hs.total_bits + 7) // 8 + sm + hs.gaps.size + 4 * hs.block_out_pos.size \
         + ed.table_bytes(cb)
-    return int(read + 2 * hs.n_weights)
+    return int(read + (2 if hs.format == 0 else 1) * hs.n_weights)
 
 
 def measured_traffic(workload: str, tile_windows: int):
@@ -119,13 +121,14 @@ def cpu_baseline(tensors, seconds_budget: float = 30.0):
 def run_unit(name, tensors, args, torch, ed):
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
-    cb = ed.df11_build_codebook(tensors)
-    hs = ed.df11_encode(cb, tensors, args.tile_windows, 8)
+    cb = ed.df11_build_codebook(tensors, args.format)
+    hs = ed.df11_encode(cb, tensors, args.tile_windows, 8, args.format)
     log(f"[bench] {name}: encoded {hs.n_weights} weights in {time.perf_counter() - t0:.1f} s, "
         f"{hs.n_tiles} tiles, luts={cb.n_luts}, max_len={cb.max_len}")
     ds = ed.DeviceStream(hs, cb, dev)
     n = hs.n_weights
-    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(n, dtype=torch.bfloat16 if args.format == "bf16" else torch.uint8,
+                      device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     alg = algorithmic_bytes(hs, cb)
@@ -155,11 +158,15 @@ def run_unit(name, tensors, args, torch, ed):
     kms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
     st = int(status.item())
-    ref = torch.from_numpy(np.concatenate([np.asarray(t).reshape(-1) for t in tensors])
-                           .view(np.int16)).to(dev)
-    exact = st == 0 and torch.equal(out.view(torch.int16), ref)
+    if args.format == "bf16":
+        ref = torch.from_numpy(np.concatenate([np.asarray(t).reshape(-1) for t in tensors])
+                               .view(np.int16)).to(dev)
+        exact = st == 0 and torch.equal(out.view(torch.int16), ref)
+    else:
+        ref = torch.from_numpy(np.concatenate([np.asarray(t).reshape(-1) for t in tensors])).to(dev)
+        exact = st == 0 and torch.equal(out, ref)
     del ref
-    payload = 8 + hs.total_bits / n
+    payload = (8 if args.format == "bf16" else 4) + hs.total_bits / n
     total_bits = 8 * (sum(hs.compressed_bytes(cb).values())) / n
     return {
         "name": name, "n": n, "hs": hs, "cb": cb, "kernel_ms": kms, "wall_s": wall,
@@ -179,6 +186,9 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes instead "
                          "(the achievable-bandwidth reference and the counter calibration)")
+    ap.add_argument("--format", default="bf16", choices=("bf16", "fp8_e4m3", "fp8_e5m2"),
+                    help="weight format of the workload (FP8: the BF16 workload quantized "
+                         "with a per-tensor scale)")
     ap.add_argument("--pipeline", action="store_true",
                     help="time the overlapped block pipeline with a GEMV consumer over the "
                          "32 blocks of the 8B model instead")
@@ -199,25 +209,34 @@ def main():
         return copy_reference(args, torch)
     if args.pipeline:
         return pipeline_bench(args, torch, ed, sw)
+    if args.format != "bf16" and (args.tile_windows != 64 or args.config in ("4",)):
+        print("FP8 workloads use 64-window tiles and single-unit configs", file=sys.stderr)
+        sys.exit(2)
     cfg = sw.config(args.config)
     if len(cfg.units) != 1:
         return stream_units(cfg, args, torch, ed, sw)
     unit = cfg.units[0]
     t0 = time.perf_counter()
-    tensors = sw.gen_unit(unit)
-    log(f"[bench] generated {cfg.name} ({unit.numel} weights) in {time.perf_counter() - t0:.1f} s")
-    r = run_unit(cfg.name, tensors, args, torch, ed)
+    if args.format == "bf16":
+        tensors = sw.gen_unit(unit)
+        workload = cfg.name
+    else:
+        tensors = sw.gen_unit_fp8(unit, args.format.split("_")[1])
+        workload = f"{cfg.name}_{args.format}"
+    log(f"[bench] generated {workload} ({unit.numel} weights) in {time.perf_counter() - t0:.1f} s")
+    r = run_unit(workload, tensors, args, torch, ed)
+    out_bytes = 2 if args.format == "bf16" else 1
     kms = r["kernel_ms"]
     avg_ms = float(kms.mean())
     n = r["n"]
     achieved = r["alg_bytes"] / (avg_ms * 1e-3) / 1e9
     if r["flushed"]:
-        value = 2 * n * args.steps / (kms.sum() * 1e-3) / 1e9  # flush kernels excluded
+        value = out_bytes * n * args.steps / (kms.sum() * 1e-3) / 1e9  # flush kernels excluded
     else:
-        value = 2 * n * args.steps / r["wall_s"] / 1e9
-    traffic = measured_traffic(cfg.name, args.tile_windows)
+        value = out_bytes * n * args.steps / r["wall_s"] / 1e9
+    traffic = measured_traffic(workload, args.tile_windows)
     line = {
-        "metric": "decompressed BF16 GB/s",
+        "metric": "decompressed BF16 GB/s" if args.format == "bf16" else "decompressed FP8 GB/s",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -230,13 +249,13 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {
-            "workload": cfg.name,
+            "workload": workload,
             "n_weights": n,
             "layout": f"T{args.tile_windows}xB8",
             "bit_exact": bool(r["exact"]),
             "bits_per_weight_payload": round(r["payload_bpw"], 4),
             "bits_per_weight_total": round(r["total_bpw"], 4),
-            "size_vs_bf16": round(r["total_bpw"] / 16, 4),
+            "size_vs_original": round(r["total_bpw"] / (8 * out_bytes), 4),
             "kernel_ms_p50": round(float(np.percentile(kms, 50)), 4),
             "kernel_ms_p99": round(float(np.percentile(kms, 99)), 4),
             "caches_flushed_between_steps": r["flushed"],
@@ -250,7 +269,7 @@ def main():
             "traffic": traffic,
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.format == "bf16":
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(tensors)
     print(json.dumps(line), flush=True)

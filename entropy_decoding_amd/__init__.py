@@ -89,6 +89,7 @@ class df11_host_stream(ctypes.Structure):
         ("n_weights", ctypes.c_uint64),
         ("total_bits", ctypes.c_uint64),
         ("n_tiles", ctypes.c_uint64),
+        ("format", ctypes.c_uint32),
     ]
 
 
@@ -109,6 +110,7 @@ class df11_device_stream(ctypes.Structure):
         ("window_bytes", ctypes.c_uint32),
         ("max_tile_symbols", ctypes.c_uint32),
         ("n_tensors", ctypes.c_uint32),
+        ("format", ctypes.c_uint32),
     ]
 
 
@@ -123,6 +125,8 @@ class df11_gemv_tensor(ctypes.Structure):
 
 
 DF11_PIPELINE_MAX_SLOTS = 4
+# df11_format; the names are what the binding's ``fmt`` arguments accept
+FORMATS = {"bf16": 0, "fp8_e4m3": 1, "fp8_e5m2": 2}
 DF11_GEMV_MAX_TENSORS = 16
 
 
@@ -136,8 +140,16 @@ def _load():
     import torch  # noqa: F401
 
     L = ctypes.CDLL(LIB_PATH)
-    tens = ctypes.POINTER(_u16p)
+    tens = ctypes.POINTER(ctypes.c_void_p)
     L.df11_build_codebook.argtypes = [tens, _u64p, ctypes.c_uint32, ctypes.POINTER(df11_codebook)]
+    L.df11_build_codebook_fmt.argtypes = [ctypes.c_uint32, tens, _u64p, ctypes.c_uint32,
+                                          ctypes.POINTER(df11_codebook)]
+    L.df11_encode_size_fmt.argtypes = [ctypes.c_uint32, ctypes.POINTER(df11_codebook), tens, _u64p,
+                                       ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                       ctypes.POINTER(df11_sizes)]
+    L.df11_encode_fmt.argtypes = [ctypes.c_uint32, ctypes.POINTER(df11_codebook), tens, _u64p,
+                                  ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                  ctypes.POINTER(df11_host_stream)]
     L.df11_encode_size.argtypes = [ctypes.POINTER(df11_codebook), tens, _u64p, ctypes.c_uint32,
                                    ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(df11_sizes)]
     L.df11_encode.argtypes = [ctypes.POINTER(df11_codebook), tens, _u64p, ctypes.c_uint32,
@@ -157,6 +169,7 @@ def _load():
     L.df11_pipeline_release.argtypes = [vp, ctypes.c_uint32, vp]
     L.df11_gemv_bf16.argtypes = [vp, ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32, vp, vp, vp]
     for f in (L.df11_build_codebook, L.df11_encode_size, L.df11_encode,
+              L.df11_build_codebook_fmt, L.df11_encode_size_fmt, L.df11_encode_fmt,
               L.df11_decompress_block, L.df11_decompress_tensor, L.df11_pipeline_create,
               L.df11_pipeline_destroy, L.df11_pipeline_decompress, L.df11_pipeline_acquire,
               L.df11_pipeline_release, L.df11_gemv_bf16):
@@ -176,17 +189,24 @@ def _check(fn: str, rc: int):
         raise Df11Error(fn, rc)
 
 
-def _tensor_args(tensors):
+def _format(fmt: str) -> int:
+    if fmt not in FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(FORMATS)}")
+    return FORMATS[fmt]
+
+
+def _tensor_args(tensors, fmt: str = "bf16"):
     if isinstance(tensors, np.ndarray):
         tensors = [tensors]
+    want = np.uint16 if fmt == "bf16" else np.uint8
     arrs = []
     for t in tensors:
         a = np.asarray(t)
-        if a.dtype != np.uint16:
-            raise TypeError("tensors must be uint16 BF16 bit patterns")
+        if a.dtype != want:
+            raise TypeError(f"{fmt} tensors must be {np.dtype(want).name} bit patterns")
         arrs.append(np.ascontiguousarray(a).reshape(-1))
     n = len(arrs)
-    ptrs = (_u16p * max(n, 1))(*[a.ctypes.data_as(_u16p) for a in arrs])
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[a.ctypes.data for a in arrs])
     numel = (ctypes.c_uint64 * max(n, 1))(*[a.size for a in arrs])
     return arrs, ptrs, numel, n
 
@@ -194,20 +214,32 @@ def _tensor_args(tensors):
 # ---------------------------------------------------------------- host calls
 
 
-def df11_build_codebook(tensors) -> df11_codebook:
-    """Histogram + Huffman (+ package-merge at 32 bits) + canonical codes + LUTs."""
-    arrs, ptrs, numel, n = _tensor_args(tensors)
+def df11_build_codebook(tensors, fmt: str = "bf16") -> df11_codebook:
+    """Histogram + Huffman (+ package-merge at 32 bits) + canonical codes + LUTs.
+    BF16 tensors are uint16 arrays (df11_build_codebook); FP8 ones uint8
+    arrays (df11_build_codebook_fmt)."""
+    arrs, ptrs, numel, n = _tensor_args(tensors, fmt)
     cb = df11_codebook()
-    _check("df11_build_codebook", LIB.df11_build_codebook(ptrs, numel, n, ctypes.byref(cb)))
+    if fmt == "bf16":
+        _check("df11_build_codebook", LIB.df11_build_codebook(ptrs, numel, n, ctypes.byref(cb)))
+    else:
+        _check("df11_build_codebook_fmt",
+               LIB.df11_build_codebook_fmt(_format(fmt), ptrs, numel, n, ctypes.byref(cb)))
     return cb
 
 
 def df11_encode_size(cb: df11_codebook, tensors, tile_windows: int = DEFAULT_TILE_WINDOWS,
-                     window_bytes: int = DEFAULT_WINDOW_BYTES) -> df11_sizes:
-    arrs, ptrs, numel, n = _tensor_args(tensors)
+                     window_bytes: int = DEFAULT_WINDOW_BYTES, fmt: str = "bf16") -> df11_sizes:
+    arrs, ptrs, numel, n = _tensor_args(tensors, fmt)
     sz = df11_sizes()
-    _check("df11_encode_size", LIB.df11_encode_size(ctypes.byref(cb), ptrs, numel, n, tile_windows,
-                                                    window_bytes, ctypes.byref(sz)))
+    if fmt == "bf16":
+        _check("df11_encode_size", LIB.df11_encode_size(ctypes.byref(cb), ptrs, numel, n,
+                                                        tile_windows, window_bytes,
+                                                        ctypes.byref(sz)))
+    else:
+        _check("df11_encode_size_fmt",
+               LIB.df11_encode_size_fmt(_format(fmt), ctypes.byref(cb), ptrs, numel, n,
+                                        tile_windows, window_bytes, ctypes.byref(sz)))
     return sz
 
 
@@ -227,6 +259,7 @@ class HostStream:
     n_weights: int
     total_bits: int
     n_tiles: int
+    format: int = 0
 
     @property
     def n_tensors(self) -> int:
@@ -236,7 +269,7 @@ class HostStream:
         """Bytes of every array a decompression reads (payload and auxiliary)."""
         d = {
             "stream": (self.total_bits + 7) // 8,
-            "sm": self.n_weights,
+            "sm": self.n_weights if self.format == 0 else (self.n_weights + 1) // 2,
             "gaps": self.gaps.size,
             "block_out_pos": 4 * self.block_out_pos.size,
         }
@@ -246,9 +279,9 @@ class HostStream:
 
 
 def df11_encode(cb: df11_codebook, tensors, tile_windows: int = DEFAULT_TILE_WINDOWS,
-                window_bytes: int = DEFAULT_WINDOW_BYTES) -> HostStream:
-    arrs, ptrs, numel, n = _tensor_args(tensors)
-    sz = df11_encode_size(cb, arrs, tile_windows, window_bytes)
+                window_bytes: int = DEFAULT_WINDOW_BYTES, fmt: str = "bf16") -> HostStream:
+    arrs, ptrs, numel, n = _tensor_args(tensors, fmt)
+    sz = df11_encode_size(cb, arrs, tile_windows, window_bytes, fmt)
     stream = np.empty(sz.stream_bytes, dtype=np.uint8)
     sm = np.empty(sz.sm_bytes, dtype=np.uint8)
     gaps = np.empty(max(1, sz.n_windows), dtype=np.uint8)
@@ -267,11 +300,16 @@ def df11_encode(cb: df11_codebook, tensors, tile_windows: int = DEFAULT_TILE_WIN
     hs.gaps_capacity = sz.n_windows
     hs.bop_capacity = bop.size
     hs.n_tensors = n
-    _check("df11_encode", LIB.df11_encode(ctypes.byref(cb), ptrs, numel, n, tile_windows,
-                                          window_bytes, ctypes.byref(hs)))
+    if fmt == "bf16":
+        _check("df11_encode", LIB.df11_encode(ctypes.byref(cb), ptrs, numel, n, tile_windows,
+                                              window_bytes, ctypes.byref(hs)))
+    else:
+        _check("df11_encode_fmt", LIB.df11_encode_fmt(_format(fmt), ctypes.byref(cb), ptrs, numel,
+                                                      n, tile_windows, window_bytes,
+                                                      ctypes.byref(hs)))
     return HostStream(stream, sm, gaps[: sz.n_windows], bop, offs, tiles[: 2 * n],
                       hs.tile_windows, hs.window_bytes, hs.max_tile_symbols, hs.n_weights,
-                      hs.total_bits, hs.n_tiles)
+                      hs.total_bits, hs.n_tiles, hs.format)
 
 
 # ---------------------------------------------------------------- device side
@@ -316,6 +354,7 @@ class DeviceStream:
         d.window_bytes = hs.window_bytes
         d.max_tile_symbols = hs.max_tile_symbols
         d.n_tensors = hs.n_tensors
+        d.format = hs.format
         self.desc = d
 
     @property
@@ -335,11 +374,17 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _check_out(ds: DeviceStream, out, n: int) -> None:
+    size = 2 if ds.desc.format == 0 else 1
+    if out.numel() < n or out.element_size() != size or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous device tensor of {n} {8 * size}-bit elements")
+
+
 def df11_decompress_block(ds: DeviceStream, out, status=None, stream=None) -> None:
     """One launch decompressing the whole unit into ``out`` (a device tensor of
-    n_weights 16-bit elements, e.g. torch.bfloat16 or torch.int16)."""
-    if out.numel() < ds.n_weights or out.element_size() != 2 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous 16-bit device tensor of n_weights elements")
+    n_weights elements: 16-bit (torch.bfloat16, torch.int16) for BF16 units,
+    8-bit (torch.uint8, torch.float8_*) for FP8 units)."""
+    _check_out(ds, out, ds.n_weights)
     sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
     _check("df11_decompress_block",
            LIB.df11_decompress_block(ctypes.byref(ds.desc), ctypes.c_void_p(out.data_ptr()), sp,
@@ -351,8 +396,7 @@ def df11_decompress_tensor(ds: DeviceStream, k: int, out, status=None, stream=No
     n = 0
     if 0 <= k < ds.tensor_offsets.size - 1:
         n = int(ds.tensor_offsets[k + 1] - ds.tensor_offsets[k])
-    if out.numel() < n or out.element_size() != 2 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous 16-bit device tensor of the tensor's numel")
+    _check_out(ds, out, n)
     sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
     _check("df11_decompress_tensor",
            LIB.df11_decompress_tensor(ctypes.byref(ds.desc), int(k),
@@ -375,8 +419,7 @@ class Pipeline:
                                         ctypes.byref(self._p)))
 
     def decompress(self, slot: int, ds: DeviceStream, out, status=None) -> None:
-        if out.numel() < ds.n_weights or out.element_size() != 2 or not out.is_contiguous():
-            raise ValueError("out must be a contiguous 16-bit device tensor of n_weights elements")
+        _check_out(ds, out, ds.n_weights)
         sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
         _check("df11_pipeline_decompress",
                LIB.df11_pipeline_decompress(self._p, int(slot), ctypes.byref(ds.desc),

@@ -77,7 +77,7 @@ struct KArgs {
     const uint8_t *gaps;
     const uint32_t *bop;
     const uint8_t *tables;
-    uint16_t *out;  // unit element i goes to out[i - out_shift]
+    void *out;  // unit element i goes to element i - out_shift (uint16 BF16 or uint8 FP8)
     int32_t *status;
     uint64_t total_bits;
     uint32_t n_weights;
@@ -353,7 +353,7 @@ __device__ __forceinline__ void store8(const KArgs &a, uint32_t gi, uint2 s8, co
     assemble4(s8.y, e8.y, v.z, v.w);
     // plain stores: with non-temporal ones the 128-byte lines that two tiles
     // share were written back twice (write traffic 5% above the output size)
-    *reinterpret_cast<uint4 *>(a.out + (gi - a.out_shift)) = v;
+    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.out) + (gi - a.out_shift)) = v;
 }
 
 // Outputs [gi, gi + 8) of the unit from 8 sm bytes and staged exponents ex[0 .. 8).
@@ -369,7 +369,8 @@ __device__ __forceinline__ void emit8(const KArgs &a, uint32_t gi, uint32_t lo, 
         for (uint32_t k = 0; k < 8; k++) {
             const uint32_t i = gi + k;
             const uint32_t sk = ((k < 4 ? s8.x : s8.y) >> (8 * (k & 3))) & 0xFFu;
-            if (i >= lo && i < hi) a.out[i - a.out_shift] = assemble1(sk, ex[k]);
+            if (i >= lo && i < hi)
+                static_cast<uint16_t *>(a.out)[i - a.out_shift] = assemble1(sk, ex[k]);
         }
     }
 }
@@ -490,10 +491,68 @@ __global__ __launch_bounds__(kThreads) void df11_decode(KArgs a) {
     }
 }
 
+// Output formats of the wave kernel.  A chunk is the outputs one lane
+// stores with one 16-byte write: 8 BF16 values or 16 FP8 values; either way
+// it takes 8 bytes of the sign+mantissa array (bytes, or nibbles two per
+// byte).  rest_off(g) is the byte offset in that array of weight g's field.
+template <int FMT>
+struct OutFmt;
+template <>
+struct OutFmt<DF11_FORMAT_BF16> {
+    static constexpr uint32_t kChunk = 8;
+    static __device__ __forceinline__ uint32_t rest_off(uint32_t g) { return g; }
+    static __device__ __forceinline__ void store(const KArgs &a, uint32_t gi, uint2 s8,
+                                                 const uint8_t *ex) {
+        store8(a, gi, s8, ex);
+    }
+    // element k (< 8) of a chunk
+    static __device__ __forceinline__ void store1(const KArgs &a, uint32_t i, uint2 s8, uint32_t k,
+                                                  uint32_t e) {
+        const uint32_t sk = ((k < 4 ? s8.x : s8.y) >> (8 * (k & 3))) & 0xFFu;
+        static_cast<uint16_t *>(a.out)[i - a.out_shift] = assemble1(sk, e);
+    }
+};
+// FP8: byte = sign << 7 | e << M | mantissa, from the nibble (sign << M | mantissa)
+template <int M>
+struct OutFp8 {
+    static constexpr uint32_t kChunk = 16;
+    static __device__ __forceinline__ uint32_t rest_off(uint32_t g) { return g >> 1; }
+    // four outputs from four nibbles (one per byte of D) and four exponents E
+    static __device__ __forceinline__ uint32_t assemble(uint32_t D, uint32_t E) {
+        constexpr uint32_t mant = 0x01010101u * ((1u << M) - 1u);
+        return (D & mant) | ((D << (7 - M)) & 0x80808080u) | (E << M);
+    }
+    // the 4 nibbles of 2 sm bytes, spread one per byte (sel picks the 2 bytes twice)
+    static __device__ __forceinline__ uint32_t spread(uint32_t S, uint32_t sel) {
+        const uint32_t u = __builtin_amdgcn_perm(S, S, sel);
+        return (u & 0x000F000Fu) | ((u >> 4) & 0x0F000F00u);
+    }
+    static __device__ __forceinline__ void store(const KArgs &a, uint32_t gi, uint2 s8,
+                                                 const uint8_t *ex) {
+        const uint4 e16 = *reinterpret_cast<const uint4 *>(ex);
+        uint4 v;
+        v.x = assemble(spread(s8.x, 0x01010000u), e16.x);
+        v.y = assemble(spread(s8.x, 0x03030202u), e16.y);
+        v.z = assemble(spread(s8.y, 0x01010000u), e16.z);
+        v.w = assemble(spread(s8.y, 0x03030202u), e16.w);
+        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.out) + (gi - a.out_shift)) = v;
+    }
+    static __device__ __forceinline__ void store1(const KArgs &a, uint32_t i, uint2 s8, uint32_t k,
+                                                  uint32_t e) {
+        const uint32_t b = ((k < 8 ? s8.x : s8.y) >> (8 * ((k >> 1) & 3))) & 0xFFu;
+        const uint32_t nib = (k & 1) ? (b >> 4) : (b & 0xFu);
+        static_cast<uint8_t *>(a.out)[i - a.out_shift] = uint8_t(assemble(nib, e));
+    }
+};
+template <>
+struct OutFmt<DF11_FORMAT_FP8_E4M3> : OutFp8<3> {};
+template <>
+struct OutFmt<DF11_FORMAT_FP8_E5M2> : OutFp8<2> {};
+
 // The 8 sm bytes of chunk c (wave-uniform, c < n8) of a tile, from the
 // registers of the lane that prefetched them, or from memory past the
 // prefetched chunks.
-template <int JP>
+template <int JP, int FMT>
 __device__ __forceinline__ uint2 chunk_sm(const KArgs &a, const uint2 (&smv)[JP], uint32_t A0,
                                           uint32_t c) {
     const uint32_t j = c >> 6, l = c & 63u;
@@ -505,7 +564,8 @@ __device__ __forceinline__ uint2 chunk_sm(const KArgs &a, const uint2 (&smv)[JP]
             r.y = __builtin_amdgcn_readlane(smv[q].y, l);
         }
     }
-    if (j >= uint32_t(JP)) r = *reinterpret_cast<const uint2 *>(a.sm + A0 + 8 * c);
+    if (j >= uint32_t(JP))
+        r = *reinterpret_cast<const uint2 *>(a.sm + OutFmt<FMT>::rest_off(A0) + 8 * c);
     return r;
 }
 
@@ -516,9 +576,12 @@ __device__ __forceinline__ uint2 chunk_sm(const KArgs &a, const uint2 (&smv)[JP]
 // take effect in issue order, so its later reads see its earlier writes.
 // Each wave has its own staging buffer.  The chunks holding a tile's first
 // and last outputs are usually shared with the neighbouring tiles; they are
-// written element by element, 8 lanes per chunk, in one pass.
-template <int JP>
+// written element by element, one lane per element, in one pass.  FMT is the
+// weight format (BF16 or FP8): only the final assembly differs.
+template <int JP, int FMT>
 __global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
+    using F = OutFmt<FMT>;
+    constexpr uint32_t CH = F::kChunk;
     __shared__ __align__(16) uint8_t fast[kLutOff];
     extern __shared__ __align__(16) uint8_t dyn[];
     constexpr uint32_t W = 64;  // windows per tile
@@ -539,14 +602,15 @@ __global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
         const uint32_t tile = a.tile0 + it;
         const uint32_t P0 = __builtin_amdgcn_readlane(cur.bounds, 0);
         const uint32_t P1 = __builtin_amdgcn_readlane(cur.bounds, 1);
-        const uint32_t A0 = P0 & ~7u;
+        const uint32_t A0 = P0 & ~(CH - 1);
         const bool sane = P0 <= P1 && P1 <= a.n_weights && P1 - A0 + 16 <= a.exp_cap;
-        const uint32_t n8 = sane ? (P1 - A0 + 7) >> 3 : 0;
+        const uint32_t n8 = sane ? (P1 - A0 + CH - 1) / CH : 0;  // chunks
+        const uint8_t *sm0 = a.sm + F::rest_off(A0);
         uint2 smv[JP];
 #pragma unroll
         for (int j = 0; j < JP; j++) {
             const uint32_t c = lane + j * 64;
-            if (c < n8) smv[j] = *reinterpret_cast<const uint2 *>(a.sm + A0 + 8 * c);
+            if (c < n8) smv[j] = *reinterpret_cast<const uint2 *>(sm0 + 8 * c);
         }
         TileIn<1> nxt;
         nxt.load<W>(a, a.tile0 + min(it + n_slots, a.n_tiles - 1), lane);
@@ -599,26 +663,24 @@ __global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
 #pragma unroll
         for (int j = 0; j < JP; j++) {
             const uint32_t c = lane + j * 64;
-            const uint32_t gi = A0 + 8 * c;
-            if (c < n8 && gi >= lo && gi + 8 <= hi) store8(a, gi, smv[j], ebuf + 8 * c);
+            const uint32_t gi = A0 + CH * c;
+            if (c < n8 && gi >= lo && gi + CH <= hi) F::store(a, gi, smv[j], ebuf + CH * c);
         }
         for (uint32_t c = lane + JP * 64; c < n8; c += 64) {
-            const uint32_t gi = A0 + 8 * c;
-            if (gi >= lo && gi + 8 <= hi)
-                store8(a, gi, *reinterpret_cast<const uint2 *>(a.sm + A0 + 8 * c), ebuf + 8 * c);
+            const uint32_t gi = A0 + CH * c;
+            if (gi >= lo && gi + CH <= hi)
+                F::store(a, gi, *reinterpret_cast<const uint2 *>(sm0 + 8 * c), ebuf + CH * c);
         }
         // the chunks holding the first and last output in range, element by
-        // element: lanes 0-7 and 8-15 (they are whole only when aligned)
+        // element: lanes 0 .. CH-1 and CH .. 2CH-1 (they are whole only when aligned)
         if (lo < hi) {
-            const uint32_t ch = (lo - A0) >> 3, ct = (hi - 1 - A0) >> 3;
-            const uint2 sh = chunk_sm<JP>(a, smv, A0, ch), sl = chunk_sm<JP>(a, smv, A0, ct);
-            if (lane < 16) {
-                const uint32_t c = lane < 8 ? ch : ct, k = lane & 7u;
-                const uint32_t gi = A0 + 8 * c, i = gi + k;
-                const bool whole = gi >= lo && gi + 8 <= hi;
-                const uint32_t sx = lane < 8 ? sh.x : sl.x, sy = lane < 8 ? sh.y : sl.y;
-                const uint32_t sk = ((k < 4 ? sx : sy) >> (8 * (k & 3))) & 0xFFu;
-                if (!whole && i >= lo && i < hi) a.out[i - a.out_shift] = assemble1(sk, ebuf[8 * c + k]);
+            const uint32_t ch = (lo - A0) / CH, ct = (hi - 1 - A0) / CH;
+            const uint2 sh = chunk_sm<JP, FMT>(a, smv, A0, ch), sl = chunk_sm<JP, FMT>(a, smv, A0, ct);
+            if (lane < 2 * CH) {
+                const uint32_t c = lane < CH ? ch : ct, k = lane & (CH - 1);
+                const uint32_t gi = A0 + CH * c, i = gi + k;
+                const bool whole = gi >= lo && gi + CH <= hi;
+                if (!whole && i >= lo && i < hi) F::store1(a, i, lane < CH ? sh : sl, k, ebuf[CH * c + k]);
             }
         }
         cur = nxt;
@@ -627,17 +689,28 @@ __global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
-const void *kernel_for(uint32_t tile_windows) {
-    if (tile_windows == 64) return reinterpret_cast<const void *>(&df11_decode_wave<4>);
+const void *kernel_for(uint32_t tile_windows, uint32_t format) {
+    if (format == DF11_FORMAT_FP8_E4M3)
+        return reinterpret_cast<const void *>(&df11_decode_wave<4, DF11_FORMAT_FP8_E4M3>);
+    if (format == DF11_FORMAT_FP8_E5M2)
+        return reinterpret_cast<const void *>(&df11_decode_wave<4, DF11_FORMAT_FP8_E5M2>);
+    if (tile_windows == 64)
+        return reinterpret_cast<const void *>(&df11_decode_wave<4, DF11_FORMAT_BF16>);
     return tile_windows == 256 ? reinterpret_cast<const void *>(&df11_decode<1, 4>)
                                : reinterpret_cast<const void *>(&df11_decode<2, 8>);
 }
+
+// Outputs per 16-byte store: 8 BF16 or 16 FP8 values.
+uint32_t chunk_outputs(uint32_t format) { return format == DF11_FORMAT_BF16 ? 8u : 16u; }
 
 // Checks shared by both entry points; fills the launch-independent fields.
 int prepare(const df11_device_stream *s, KArgs &a) {
     if (!s) return DF11_E_INVALID;
     if (s->window_bytes != 8 ||
         (s->tile_windows != 64 && s->tile_windows != 256 && s->tile_windows != 512))
+        return DF11_E_INVALID;
+    if (s->format > DF11_FORMAT_FP8_E5M2 ||
+        (s->format != DF11_FORMAT_BF16 && s->tile_windows != 64))
         return DF11_E_INVALID;
     if (s->n_weights >= (uint64_t(1) << 32)) return DF11_E_INVALID;
     const uint64_t tile_bits = uint64_t(64) * s->tile_windows;
@@ -664,8 +737,9 @@ int prepare(const df11_device_stream *s, KArgs &a) {
     a.lds_tables = kLutOff + 512u * (s->n_luts - 1);
     // dynamic LDS: hierarchical tables, 16 bytes of wave totals, staging
     a.ebuf_off = 512u * a.lut_last + 16;
-    // outputs from P0 & ~7 to the last 8-chunk, plus the 2 spill bytes
-    a.exp_cap = (s->max_tile_symbols + 7 + 16 + 15) & ~15u;
+    // outputs from P0 rounded down to a chunk to the last chunk, plus the 2 spill bytes
+    const uint32_t chunk = chunk_outputs(s->format);
+    a.exp_cap = (s->max_tile_symbols + (chunk - 1) + 16 + 15) & ~15u;
     return DF11_OK;
 }
 
@@ -675,7 +749,7 @@ int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t 
     // one staging buffer per workgroup, or one per wave for 64-window tiles
     const uint32_t per_wg = s->tile_windows == 64 ? 4u : 1u;
     const size_t lds = size_t(a.ebuf_off) + size_t(a.exp_cap) * per_wg;
-    const void *fn = kernel_for(s->tile_windows);
+    const void *fn = kernel_for(s->tile_windows, s->format);
     if (lds > 65536 &&
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
         return DF11_E_INVALID;
@@ -700,7 +774,7 @@ int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t 
 
 extern "C" {
 
-int df11_decompress_block(const df11_device_stream *s, uint16_t *out, int32_t *d_status,
+int df11_decompress_block(const df11_device_stream *s, void *out, int32_t *d_status,
                           df11_hip_stream st) {
     KArgs a{};
     int rc = prepare(s, a);
@@ -715,14 +789,15 @@ int df11_decompress_block(const df11_device_stream *s, uint16_t *out, int32_t *d
     return launch(s, a, uint32_t(s->n_tiles), static_cast<hipStream_t>(st));
 }
 
-int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, uint16_t *out,
+int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, void *out,
                            int32_t *d_status, df11_hip_stream st) {
     KArgs a{};
     int rc = prepare(s, a);
     if (rc != DF11_OK) return rc;
     if (k >= s->n_tensors || !s->tensor_offsets || !s->tensor_tiles) return DF11_E_INVALID;
     const uint64_t off = s->tensor_offsets[k], end = s->tensor_offsets[k + 1];
-    if (end < off || end > s->n_weights || (off & 7)) return DF11_E_INVALID;
+    if (end < off || end > s->n_weights || (off & (chunk_outputs(s->format) - 1)))
+        return DF11_E_INVALID;
     if (end == off) return DF11_OK;
     if (!out || !aligned(out, 16)) return DF11_E_INVALID;
     const uint64_t t0 = s->tensor_tiles[2 * k], t1 = s->tensor_tiles[2 * k + 1];

@@ -46,45 +46,90 @@ void parallel_for(size_t n, F &&f) {
     for (auto &th : pool) th.join();
 }
 
+// Weight formats.  The coded symbol is the exponent field; the sign and
+// mantissa are stored raw: one byte per BF16 weight, one nibble per FP8
+// weight (sign just above the mantissa, two per byte, lower index in the low
+// nibble).
+struct BF16 {
+    using T = uint16_t;
+    static constexpr bool kNibbles = false;
+    static uint32_t sym(T x) { return (x >> 7) & 0xFF; }
+    static uint32_t rest(T x) { return ((x >> 8) & 0x80) | (x & 0x7F); }
+};
+struct E4M3 {
+    using T = uint8_t;
+    static constexpr bool kNibbles = true;
+    static uint32_t sym(T x) { return (x >> 3) & 0xF; }
+    static uint32_t rest(T x) { return ((x >> 4) & 0x8) | (x & 0x7); }
+};
+struct E5M2 {
+    using T = uint8_t;
+    static constexpr bool kNibbles = true;
+    static uint32_t sym(T x) { return (x >> 2) & 0x1F; }
+    static uint32_t rest(T x) { return ((x >> 5) & 0x4) | (x & 0x3); }
+};
+
+// Calls f with the traits of a format; false for an unknown format.
+template <class F>
+bool with_format(uint32_t format, F &&f) {
+    switch (format) {
+    case DF11_FORMAT_BF16: f(BF16{}); return true;
+    case DF11_FORMAT_FP8_E4M3: f(E4M3{}); return true;
+    case DF11_FORMAT_FP8_E5M2: f(E5M2{}); return true;
+    default: return false;
+    }
+}
+
+uint32_t element_bytes(uint32_t format) { return format == DF11_FORMAT_BF16 ? 2u : 1u; }
+
 struct Piece {
-    const uint16_t *w;
+    const void *w;   // first element of the piece
     uint64_t count;
     uint64_t begin;  // global weight index
     uint32_t tensor;
 };
 
-std::vector<Piece> split(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n) {
+std::vector<Piece> split(uint32_t format, const void *const *tensors, const uint64_t *numel,
+                         uint32_t n) {
     std::vector<Piece> out;
+    const uint32_t eb = element_bytes(format);
     uint64_t g = 0;
     for (uint32_t k = 0; k < n; k++) {
         for (uint64_t o = 0; o < numel[k]; o += kChunk)
-            out.push_back({tensors[k] + o, std::min(kChunk, numel[k] - o), g + o, k});
+            out.push_back({static_cast<const uint8_t *>(tensors[k]) + o * eb,
+                           std::min(kChunk, numel[k] - o), g + o, k});
         g += numel[k];
     }
     return out;
 }
 
 // Exponent histogram over all pieces, one partial table per piece.
+template <class Fm>
 void histogram(const std::vector<Piece> &pieces, std::vector<uint64_t> &per_piece,
                uint64_t total[kSyms]) {
     per_piece.assign(pieces.size() * kSyms, 0);
     parallel_for(pieces.size(), [&](size_t p) {
         uint32_t h[4][kSyms] = {};
-        const uint16_t *w = pieces[p].w;
+        const auto *w = static_cast<const typename Fm::T *>(pieces[p].w);
         uint64_t n = pieces[p].count, i = 0;
         for (; i + 4 <= n; i += 4) {
-            h[0][(w[i] >> 7) & 0xFF]++;
-            h[1][(w[i + 1] >> 7) & 0xFF]++;
-            h[2][(w[i + 2] >> 7) & 0xFF]++;
-            h[3][(w[i + 3] >> 7) & 0xFF]++;
+            h[0][Fm::sym(w[i])]++;
+            h[1][Fm::sym(w[i + 1])]++;
+            h[2][Fm::sym(w[i + 2])]++;
+            h[3][Fm::sym(w[i + 3])]++;
         }
-        for (; i < n; i++) h[0][(w[i] >> 7) & 0xFF]++;
+        for (; i < n; i++) h[0][Fm::sym(w[i])]++;
         uint64_t *dst = &per_piece[p * kSyms];
         for (int s = 0; s < kSyms; s++) dst[s] = uint64_t(h[0][s]) + h[1][s] + h[2][s] + h[3][s];
     });
     std::fill(total, total + kSyms, 0);
     for (size_t p = 0; p < pieces.size(); p++)
         for (int s = 0; s < kSyms; s++) total[s] += per_piece[p * kSyms + s];
+}
+
+void histogram_any(uint32_t format, const std::vector<Piece> &pieces,
+                   std::vector<uint64_t> &per_piece, uint64_t total[kSyms]) {
+    with_format(format, [&](auto fm) { histogram<decltype(fm)>(pieces, per_piece, total); });
 }
 
 // ---------------------------------------------------------------- lengths
@@ -289,6 +334,12 @@ void build_multi_tables(df11_codebook *cb) {
 
 bool valid_layout(uint32_t T, uint32_t B) { return B == 8 && (T == 64 || T == 256 || T == 512); }
 
+// FP8 units are decoded by the 64-window kernel only.
+bool valid_format_layout(uint32_t format, uint32_t T) {
+    if (format == DF11_FORMAT_BF16) return true;
+    return (format == DF11_FORMAT_FP8_E4M3 || format == DF11_FORMAT_FP8_E5M2) && T == 64;
+}
+
 int log2u(uint64_t x) {
     int r = 0;
     while ((uint64_t(1) << r) < x) r++;
@@ -302,8 +353,8 @@ bool valid_codebook(const df11_codebook *cb) {
     return true;
 }
 
-int sizes_from_counts(const df11_codebook *cb, const uint64_t counts[kSyms], uint64_t n,
-                      uint32_t T, uint32_t B, df11_sizes *out) {
+int sizes_from_counts(uint32_t format, const df11_codebook *cb, const uint64_t counts[kSyms],
+                      uint64_t n, uint32_t T, uint32_t B, df11_sizes *out) {
     uint64_t bits = 0;
     for (int s = 0; s < kSyms; s++) {
         if (counts[s] && !cb->code_len[s]) return DF11_E_SYMBOL;
@@ -315,12 +366,13 @@ int sizes_from_counts(const df11_codebook *cb, const uint64_t counts[kSyms], uin
     out->n_tiles = (bits + tile_bits - 1) / tile_bits;
     out->n_windows = out->n_tiles * T;
     out->stream_bytes = out->n_tiles * T * B + DF11_STREAM_PAD;
-    out->sm_bytes = (n + 63) / 64 * 64 + 64;
+    const uint64_t rest_bytes = format == DF11_FORMAT_BF16 ? n : (n + 1) / 2;
+    out->sm_bytes = (rest_bytes + 63) / 64 * 64 + 64;
     out->bop_entries = out->n_tiles + 1;
     return DF11_OK;
 }
 
-bool bad_inputs(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n) {
+bool bad_inputs(const void *const *tensors, const uint64_t *numel, uint32_t n) {
     if (n && (!tensors || !numel)) return true;
     for (uint32_t k = 0; k < n; k++)
         if (numel[k] && !tensors[k]) return true;
@@ -338,6 +390,7 @@ inline void or_byte(uint8_t *p, uint8_t v) {
 }
 
 // Encodes one piece whose first code starts at bit `pos`.
+template <class Fm>
 void encode_piece(const df11_codebook *cb, const Piece &pc, uint64_t pos, uint64_t end_pos,
                   int wshift, int tshift, uint8_t *stream, uint8_t *sm, uint8_t *gaps,
                   uint32_t *bop, PieceOut &po) {
@@ -353,11 +406,11 @@ void encode_piece(const df11_codebook *cb, const Piece &pc, uint64_t pos, uint64
     uint64_t last_window = po.first_window;
     uint64_t next_tile = ((pos >> tshift) + 1) << tshift;
 
-    const uint16_t *w = pc.w;
-    uint8_t *smo = sm + pc.begin;
+    const auto *w = static_cast<const typename Fm::T *>(pc.w);
+    uint32_t pend = 0;  // FP8: the low nibble waiting for its pair
     for (uint64_t i = 0; i < pc.count; i++) {
-        const uint32_t x = w[i];
-        const uint32_t e = (x >> 7) & 0xFF;
+        const auto x = w[i];
+        const uint32_t e = Fm::sym(x);
         if (pos >= next_window) {  // first code starting in a new window
             last_window = pos >> wshift;
             gaps[last_window] = uint8_t(pos & wmask);
@@ -386,7 +439,22 @@ void encode_piece(const df11_codebook *cb, const Piece &pc, uint64_t pos, uint64
             nacc -= 32;
             acc &= (uint64_t(1) << nacc) - 1;
         }
-        smo[i] = uint8_t(((x >> 8) & 0x80) | (x & 0x7F));
+        if constexpr (!Fm::kNibbles) {
+            sm[pc.begin + i] = uint8_t(Fm::rest(x));
+        } else {
+            const uint64_t g = pc.begin + i;
+            if (g & 1) {
+                const uint8_t v = uint8_t(pend | (Fm::rest(x) << 4));
+                if (i == 0) or_byte(sm + (g >> 1), v);  // low nibble from the piece before
+                else sm[g >> 1] = v;
+            } else {
+                pend = Fm::rest(x);
+            }
+        }
+    }
+    if constexpr (Fm::kNibbles) {
+        const uint64_t g = pc.begin + pc.count;  // one past the last weight
+        if (pc.count && (g & 1)) or_byte(sm + (g >> 1), uint8_t(pend));  // high nibble from the next
     }
     // tail bytes, the last possibly shared with the next piece
     for (unsigned k = 0; k < nacc; k += 8) {
@@ -419,14 +487,15 @@ const char *df11_status_string(int status) {
     }
 }
 
-int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n_tensors,
-                        df11_codebook *cb) {
+int df11_build_codebook_fmt(uint32_t format, const void *const *tensors, const uint64_t *numel,
+                            uint32_t n_tensors, df11_codebook *cb) {
     try {
-        if (!cb || bad_inputs(tensors, numel, n_tensors)) return DF11_E_INVALID;
-        auto pieces = split(tensors, numel, n_tensors);
+        if (!cb || bad_inputs(tensors, numel, n_tensors) || !with_format(format, [](auto) {}))
+            return DF11_E_INVALID;
+        auto pieces = split(format, tensors, numel, n_tensors);
         std::vector<uint64_t> per;
         uint64_t counts[kSyms];
-        histogram(pieces, per, counts);
+        histogram_any(format, pieces, per, counts);
         uint64_t n = 0;
         for (int s = 0; s < kSyms; s++) n += counts[s];
         if (n == 0) return DF11_E_INVALID;
@@ -444,42 +513,56 @@ int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel, u
     }
 }
 
-int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors, const uint64_t *numel,
-                     uint32_t n_tensors, uint32_t tile_windows, uint32_t window_bytes,
-                     df11_sizes *out) {
+int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n_tensors,
+                        df11_codebook *cb) {
+    return df11_build_codebook_fmt(DF11_FORMAT_BF16, reinterpret_cast<const void *const *>(tensors),
+                                   numel, n_tensors, cb);
+}
+
+int df11_encode_size_fmt(uint32_t format, const df11_codebook *cb, const void *const *tensors,
+                         const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
+                         uint32_t window_bytes, df11_sizes *out) {
     try {
         if (!cb || !out || bad_inputs(tensors, numel, n_tensors) ||
-            !valid_layout(tile_windows, window_bytes) || !valid_codebook(cb))
+            !valid_layout(tile_windows, window_bytes) || !valid_codebook(cb) ||
+            !valid_format_layout(format, tile_windows))
             return DF11_E_INVALID;
-        auto pieces = split(tensors, numel, n_tensors);
+        auto pieces = split(format, tensors, numel, n_tensors);
         std::vector<uint64_t> per;
         uint64_t counts[kSyms];
-        histogram(pieces, per, counts);
+        histogram_any(format, pieces, per, counts);
         uint64_t n = 0;
         for (uint32_t k = 0; k < n_tensors; k++) n += numel[k];
-        return sizes_from_counts(cb, counts, n, tile_windows, window_bytes, out);
+        return sizes_from_counts(format, cb, counts, n, tile_windows, window_bytes, out);
     } catch (...) {
         return DF11_E_INVALID;
     }
 }
 
-int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const uint64_t *numel,
-                uint32_t n_tensors, uint32_t tile_windows, uint32_t window_bytes,
-                df11_host_stream *out) {
+int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors, const uint64_t *numel,
+                     uint32_t n_tensors, uint32_t tile_windows, uint32_t window_bytes,
+                     df11_sizes *out) {
+    return df11_encode_size_fmt(DF11_FORMAT_BF16, cb, reinterpret_cast<const void *const *>(tensors),
+                                numel, n_tensors, tile_windows, window_bytes, out);
+}
+
+int df11_encode_fmt(uint32_t format, const df11_codebook *cb, const void *const *tensors,
+                    const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
+                    uint32_t window_bytes, df11_host_stream *out) {
     try {
         if (!cb || !out || bad_inputs(tensors, numel, n_tensors) ||
             !valid_layout(tile_windows, window_bytes) || !valid_codebook(cb) ||
-            out->n_tensors != n_tensors)
+            !valid_format_layout(format, tile_windows) || out->n_tensors != n_tensors)
             return DF11_E_INVALID;
-        auto pieces = split(tensors, numel, n_tensors);
+        auto pieces = split(format, tensors, numel, n_tensors);
         std::vector<uint64_t> per;
         uint64_t counts[kSyms];
-        histogram(pieces, per, counts);
+        histogram_any(format, pieces, per, counts);
         uint64_t n = 0;
         for (uint32_t k = 0; k < n_tensors; k++) n += numel[k];
         if (n >= (uint64_t(1) << 32)) return DF11_E_INVALID;
         df11_sizes sz;
-        int rc = sizes_from_counts(cb, counts, n, tile_windows, window_bytes, &sz);
+        int rc = sizes_from_counts(format, cb, counts, n, tile_windows, window_bytes, &sz);
         if (rc != DF11_OK) return rc;
         if (!out->stream || !out->sm || !out->block_out_pos || !out->tensor_offsets ||
             (n_tensors && !out->tensor_tiles) || (sz.n_windows && !out->gaps))
@@ -500,14 +583,18 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const u
 
         std::memset(out->stream, 0, sz.stream_bytes);
         std::memset(out->gaps, 255, sz.n_windows);
-        std::memset(out->sm + n, 0, sz.sm_bytes - n);
+        if (format == DF11_FORMAT_BF16) std::memset(out->sm + n, 0, sz.sm_bytes - n);
+        else std::memset(out->sm, 0, sz.sm_bytes);  // nibbles of neighbouring pieces are OR-ed
         out->block_out_pos[0] = 0;
         out->block_out_pos[sz.n_tiles] = uint32_t(n);
 
         std::vector<PieceOut> po(pieces.size());
-        parallel_for(pieces.size(), [&](size_t p) {
-            encode_piece(cb, pieces[p], start[p], start[p + 1], wshift, tshift, out->stream,
-                         out->sm, out->gaps, out->block_out_pos, po[p]);
+        with_format(format, [&](auto fm) {
+            parallel_for(pieces.size(), [&](size_t p) {
+                encode_piece<decltype(fm)>(cb, pieces[p], start[p], start[p + 1], wshift, tshift,
+                                           out->stream, out->sm, out->gaps, out->block_out_pos,
+                                           po[p]);
+            });
         });
         // a piece's first window may already have a code start from the piece before
         bool have_prev = false;
@@ -529,8 +616,12 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const u
                 if (pieces[p].tensor == k) bits_k += start[p + 1] - start[p];
             out->tensor_tiles[2 * k] = bit >> tshift;
             if (numel[k]) {
-                const uint16_t last = tensors[k][numel[k] - 1];
-                const uint64_t last_start = bit + bits_k - cb->code_len[(last >> 7) & 0xFF];
+                uint32_t last_sym = 0;
+                with_format(format, [&](auto fm) {
+                    using Fm = decltype(fm);
+                    last_sym = Fm::sym(static_cast<const typename Fm::T *>(tensors[k])[numel[k] - 1]);
+                });
+                const uint64_t last_start = bit + bits_k - cb->code_len[last_sym];
                 out->tensor_tiles[2 * k + 1] = (last_start >> tshift) + 1;
             } else {
                 out->tensor_tiles[2 * k + 1] = out->tensor_tiles[2 * k];
@@ -549,10 +640,18 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const u
         out->n_weights = n;
         out->total_bits = sz.total_bits;
         out->n_tiles = sz.n_tiles;
+        out->format = format;
         return DF11_OK;
     } catch (...) {
         return DF11_E_INVALID;
     }
+}
+
+int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const uint64_t *numel,
+                uint32_t n_tensors, uint32_t tile_windows, uint32_t window_bytes,
+                df11_host_stream *out) {
+    return df11_encode_fmt(DF11_FORMAT_BF16, cb, reinterpret_cast<const void *const *>(tensors),
+                           numel, n_tensors, tile_windows, window_bytes, out);
 }
 
 }  // extern "C"

@@ -198,7 +198,7 @@ int df11_pipeline_destroy(df11_pipeline *p) {
 }
 
 int df11_pipeline_decompress(df11_pipeline *p, uint32_t slot, const df11_device_stream *s,
-                             uint16_t *out, int32_t *d_status) {
+                             void *out, int32_t *d_status) {
     if (!p || slot >= p->n_slots) return DF11_E_INVALID;
     // the slot's previous contents must have been released by their consumer
     if (p->was_released[slot] && hipStreamWaitEvent(p->decode, p->released[slot], 0) != hipSuccess)

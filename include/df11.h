@@ -66,6 +66,27 @@ typedef enum df11_status {
 /* An opaque hipStream_t (0 = the null stream). */
 typedef void *df11_hip_stream;
 
+/*
+ * Weight formats.  The coded symbol is always the exponent field; the sign
+ * and mantissa bits are stored raw.  FP8 follows "To Compress or Not? ...
+ * Exponent Concentration", abstract (FP8 weight exponents are concentrated
+ * too); the pages give no layout, so these are readings of the OCP 8-bit
+ * formats:
+ *   DF11_FORMAT_BF16      16-bit weights: symbol (w >> 7) & 0xFF, one sm byte
+ *                         ((w >> 8) & 0x80) | (w & 0x7F) per weight
+ *   DF11_FORMAT_FP8_E4M3  8-bit weights: symbol (b >> 3) & 0xF, one nibble
+ *                         (sign << 3) | (b & 7) per weight
+ *   DF11_FORMAT_FP8_E5M2  8-bit weights: symbol (b >> 2) & 0x1F, one nibble
+ *                         (sign << 2) | (b & 3) per weight
+ * Nibbles are stored two per byte, the lower-indexed weight in the low
+ * nibble.  FP8 units use 64-window tiles (T = 64).
+ */
+typedef enum df11_format {
+    DF11_FORMAT_BF16 = 0,
+    DF11_FORMAT_FP8_E4M3 = 1,
+    DF11_FORMAT_FP8_E5M2 = 2
+} df11_format;
+
 #define DF11_MULTI_BITS 10      /* index width of the multi-symbol decode table */
 #define DF11_COUNT_BITS 12      /* index width of the code-start (count) table */
 
@@ -120,7 +141,7 @@ typedef struct df11_sizes {
     uint64_t n_tiles;        /* ceil(total_bits / (8 * B * T)) */
     uint64_t n_windows;      /* n_tiles * T: bytes of gaps */
     uint64_t stream_bytes;   /* n_tiles * T * B + DF11_STREAM_PAD */
-    uint64_t sm_bytes;       /* N rounded up to 64, plus 64 bytes of padding */
+    uint64_t sm_bytes;       /* N (BF16) or ceil(N / 2) (FP8) rounded up to 64, plus 64 bytes */
     uint64_t bop_entries;    /* n_tiles + 1 entries of block_out_pos */
 } df11_sizes;
 
@@ -145,6 +166,7 @@ typedef struct df11_host_stream {
     uint64_t n_weights;
     uint64_t total_bits;
     uint64_t n_tiles;
+    uint32_t format;            /* df11_format of the weights */
 } df11_host_stream;
 
 /*
@@ -171,6 +193,7 @@ typedef struct df11_device_stream {
     uint32_t window_bytes;
     uint32_t max_tile_symbols;
     uint32_t n_tensors;
+    uint32_t format;            /* df11_format; 0 (BF16) when zero-initialised */
 } df11_device_stream;
 
 /*
@@ -189,6 +212,12 @@ typedef struct df11_device_stream {
 int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel,
                         uint32_t n_tensors, df11_codebook *cb);
 
+/* The same for any df11_format: tensors[k] points to numel[k] weights of
+ * that format (uint16_t for BF16, uint8_t for FP8).  DF11_E_INVALID for an
+ * unknown format. */
+int df11_build_codebook_fmt(uint32_t format, const void *const *tensors, const uint64_t *numel,
+                            uint32_t n_tensors, df11_codebook *cb);
+
 /*
  * df11_encode_size -- host.  Sizes of all arrays df11_encode will write for
  * these tensors under layout (tile_windows T, window_bytes B).  Supported
@@ -197,6 +226,11 @@ int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel,
 int df11_encode_size(const df11_codebook *cb, const uint16_t *const *tensors,
                      const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
                      uint32_t window_bytes, df11_sizes *out);
+
+/* df11_encode_size for any df11_format (FP8 requires T = 64). */
+int df11_encode_size_fmt(uint32_t format, const df11_codebook *cb, const void *const *tensors,
+                         const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
+                         uint32_t window_bytes, df11_sizes *out);
 
 /*
  * df11_encode -- host, offline.  Writes the concatenated exponent code stream,
@@ -211,19 +245,25 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors,
                 const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
                 uint32_t window_bytes, df11_host_stream *out);
 
+/* df11_encode for any df11_format (FP8 requires T = 64); out->format is set. */
+int df11_encode_fmt(uint32_t format, const df11_codebook *cb, const void *const *tensors,
+                    const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
+                    uint32_t window_bytes, df11_host_stream *out);
+
 /*
  * df11_decompress_block -- device.  Transformer-block-level decompression
  * (DFloat11 abstract): the whole unit in exactly one kernel launch, on stream
- * st, into out[0 .. n_weights) (device memory, 16-byte aligned, caller-owned;
- * tensor k is out[tensor_offsets[k] .. tensor_offsets[k+1])).  Every output
- * equals the original BF16 bit pattern.  Asynchronous: returns after the
+ * st, into out[0 .. n_weights) (device memory, 16-byte aligned, caller-owned,
+ * uint16_t elements for BF16 and uint8_t for FP8 units; tensor k is
+ * out[tensor_offsets[k] .. tensor_offsets[k+1])).  Every output equals the
+ * original bit pattern.  Asynchronous: returns after the
  * launch.  Synchronous errors: DF11_E_INVALID (null or misaligned pointers,
  * unsupported layout, sizes inconsistent with each other), DF11_E_HIP.  The
  * kernel checks each tile's decoded symbol count against block_out_pos and,
  * on a mismatch, writes DF11_E_CORRUPT to *d_status (device int32, may be
  * null) and leaves that tile's outputs unwritten.  N == 0 launches nothing.
  */
-int df11_decompress_block(const df11_device_stream *s, uint16_t *out, int32_t *d_status,
+int df11_decompress_block(const df11_device_stream *s, void *out, int32_t *d_status,
                           df11_hip_stream st);
 
 /*
@@ -231,9 +271,10 @@ int df11_decompress_block(const df11_device_stream *s, uint16_t *out, int32_t *d
  * into out[0 .. numel_k) (device, 16-byte aligned) with one launch over the
  * tiles that hold its codes; same kernel, checks and errors as
  * df11_decompress_block.  The tensor's element offset in the unit must be a
- * multiple of 8 (DF11_E_INVALID otherwise; decompress the block instead).
+ * multiple of 8 for BF16 and of 16 for FP8 units (DF11_E_INVALID otherwise;
+ * decompress the block instead).
  */
-int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, uint16_t *out,
+int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, void *out,
                            int32_t *d_status, df11_hip_stream st);
 
 /* Static description of a status code. */
@@ -276,7 +317,7 @@ int df11_pipeline_destroy(df11_pipeline *p);
  * ready event.  Same argument errors as df11_decompress_block.  A slot that a
  * consumer has read must be released before it is refilled. */
 int df11_pipeline_decompress(df11_pipeline *p, uint32_t slot, const df11_device_stream *s,
-                             uint16_t *out, int32_t *d_status);
+                             void *out, int32_t *d_status);
 
 /* Makes the consumer stream wait until the slot's latest decompression is
  * done.  DF11_E_INVALID if the slot was never filled. */

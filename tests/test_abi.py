@@ -51,6 +51,9 @@ int main(void) {{
          offsetof(df11_device_stream, n_luts));
   printf("%zu %zu %zu %d %d\\n", sizeof(df11_gemv_tensor), offsetof(df11_gemv_tensor, rows),
          offsetof(df11_gemv_tensor, cols), DF11_PIPELINE_MAX_SLOTS, DF11_GEMV_MAX_TENSORS);
+  printf("%zu %zu %d %d %d\\n", offsetof(df11_host_stream, format),
+         offsetof(df11_device_stream, format), DF11_FORMAT_BF16, DF11_FORMAT_FP8_E4M3,
+         DF11_FORMAT_FP8_E5M2);
   return 0;
 }}
 '''
@@ -72,6 +75,9 @@ int main(void) {{
     assert g == [ctypes.sizeof(ed.df11_gemv_tensor), ed.df11_gemv_tensor.rows.offset,
                  ed.df11_gemv_tensor.cols.offset, ed.DF11_PIPELINE_MAX_SLOTS,
                  ed.DF11_GEMV_MAX_TENSORS]
+    f = [int(x) for x in lines[3].split()]
+    assert f == [ed.df11_host_stream.format.offset, ed.df11_device_stream.format.offset,
+                 ed.FORMATS["bf16"], ed.FORMATS["fp8_e4m3"], ed.FORMATS["fp8_e5m2"]]
 
 
 def test_status_strings():

@@ -11,6 +11,7 @@ import pytest
 
 import entropy_decoding_amd as ed
 import oracle
+import synth_weights as sw
 
 
 def _compare(tensors, threads=512, bpt=8, expect_same_lengths=True):
@@ -241,3 +242,65 @@ def test_fast_tables_match_a_brute_force_decode(which, unit_tensors):
             continue
         assert e & 0xFFF == sum(1 << pos for pos, _, _ in got), x
     assert (n_long > 0) == (int(lens.max()) > kM)
+
+
+# ------------------------------------------------------------------ FP8 units
+
+
+def _fp8(w16, fmt, scale=20000.0):
+    return sw.fp8_from_f32((w16.astype(np.uint32) << 16).view(np.float32) * np.float32(scale), fmt)
+
+
+def _compare_fp8(tensors, fmt):
+    """Library FP8 encoding vs the oracle, byte for byte."""
+    of = fmt.split("_")[1]
+    cb = ed.df11_build_codebook(tensors, fmt)
+    hs = ed.df11_encode(cb, tensors, 64, 8, fmt)
+    allb = np.concatenate([np.asarray(t, np.uint8).reshape(-1) for t in tensors])
+    sym, sm = oracle.fp8_split(allb, of)
+    ocb = oracle.codebook_symbols(sym)
+    lens, codes = ed.codebook_arrays(cb)
+    assert np.array_equal(lens, ocb.lens) and np.array_equal(codes[lens > 0], ocb.codes[lens > 0])
+    stream, total = oracle.encode_symbols(sym, ocb)
+    assert hs.total_bits == total and hs.format == ed.FORMATS[fmt]
+    assert np.array_equal(hs.stream[:stream.size], stream) and not hs.stream[stream.size:].any()
+    assert np.array_equal(hs.sm[:sm.size], sm) and not hs.sm[sm.size:].any()
+    gaps, bop = oracle.aux_symbols(sym, ocb, 64, 8)
+    assert np.array_equal(hs.gaps, gaps) and np.array_equal(hs.block_out_pos, bop)
+    assert hs.max_tile_symbols == int(np.diff(bop.astype(np.int64)).max())
+    return cb, hs
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "fp8_e5m2"])
+def test_fp8_units_match_oracle(fmt, unit_tensors):
+    (w,) = unit_tensors("0")
+    b = _fp8(w, fmt.split("_")[1])
+    _compare_fp8([b], fmt)
+    # odd-sized tensors: sign+mantissa bytes shared by two tensors, and pieces of
+    # more than 4 Mi weights starting at odd indices
+    rng = np.random.default_rng(21)
+    big = rng.integers(0, 256, (1 << 22) + 5001, dtype=np.uint8) & np.uint8(0xC7) | np.uint8(0x30)
+    _compare_fp8([b[:333_333], b[333_333:], big, b[:7]], fmt)
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "fp8_e5m2"])
+def test_fp8_every_byte_value(fmt):
+    b = np.tile(np.arange(256, dtype=np.uint8), 50)
+    np.random.default_rng(4).shuffle(b)
+    _compare_fp8([b], fmt)
+
+
+def test_fp8_argument_errors():
+    b = np.arange(256, dtype=np.uint8)
+    cb = ed.df11_build_codebook([b], "fp8_e4m3")
+    with pytest.raises(ed.Df11Error) as e:
+        ed.df11_encode(cb, [b], 256, 8, "fp8_e4m3")  # FP8 units use 64-window tiles
+    assert e.value.status == ed.DF11_E_INVALID
+    with pytest.raises(TypeError):
+        ed.df11_build_codebook([b.astype(np.uint16)], "fp8_e4m3")
+    with pytest.raises(ValueError):
+        ed.df11_build_codebook([b], "fp8_e3m4")
+    ptrs = (ed.ctypes.c_void_p * 1)(b.ctypes.data)
+    numel = (ed.ctypes.c_uint64 * 1)(b.size)
+    rc = ed.LIB.df11_build_codebook_fmt(7, ptrs, numel, 1, ed.ctypes.byref(ed.df11_codebook()))
+    assert rc == ed.DF11_E_INVALID
