@@ -189,6 +189,8 @@ def main():
     ap.add_argument("--format", default="bf16", choices=("bf16", "fp8_e4m3", "fp8_e5m2"),
                     help="weight format of the workload (FP8: the BF16 workload quantized "
                          "with a per-tensor scale)")
+    ap.add_argument("--encode", action="store_true",
+                    help="time the GPU-side encoder (and the host encoder) on the workload instead")
     ap.add_argument("--pipeline", action="store_true",
                     help="time the overlapped block pipeline with a GEMV consumer over the "
                          "32 blocks of the 8B model instead")
@@ -209,6 +211,8 @@ def main():
         return copy_reference(args, torch)
     if args.pipeline:
         return pipeline_bench(args, torch, ed, sw)
+    if args.encode:
+        return encode_bench(args, torch, ed, sw)
     if args.format != "bf16" and (args.tile_windows != 64 or args.config in ("4",)):
         print("FP8 workloads use 64-window tiles and single-unit configs", file=sys.stderr)
         sys.exit(2)
@@ -369,6 +373,87 @@ def stream_units(cfg, args, torch, ed, sw):
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+    if not exact:
+        sys.exit(1)
+
+
+def encode_bench(args, torch, ed, sw):
+    """The GPU-side encoder on a single-unit workload: device histogram, host
+    codebook from it, device encode; timed with HIP events on one stream, the
+    host encoder timed beside it.  Output arrays are compared with the host's."""
+    import ctypes
+
+    dev = torch.device("cuda:0")
+    cfg = sw.config(args.config)
+    unit = cfg.units[0]
+    fmt = args.format
+    tensors = sw.gen_unit(unit) if fmt == "bf16" else sw.gen_unit_fp8(unit, fmt.split("_")[1])
+    flat = np.concatenate([t.reshape(-1) for t in tensors])
+    n = flat.size
+    w = torch.from_numpy(flat.view(np.int16) if fmt == "bf16" else flat).to(dev)
+    stream = torch.cuda.current_stream()
+    # sizes and buffers once (the codebook is the same for every step)
+    counts = ed.df11_histogram_device(w, fmt).cpu().numpy().view(np.uint64)
+    t0 = time.perf_counter()
+    cb = ed.df11_build_codebook_from_counts(counts)
+    codebook_ms = (time.perf_counter() - t0) * 1e3
+    sz = ed.df11_sizes()
+    ed._check("df11_encode_size_from_counts", ed.LIB.df11_encode_size_from_counts(
+        ed.FORMATS[fmt], ctypes.byref(cb), counts.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+        n, args.tile_windows, 8, ctypes.byref(sz)))
+    bufs = [torch.empty(x, dtype=torch.uint8, device=dev)
+            for x in (sz.stream_bytes, sz.sm_bytes, max(16, sz.n_windows), 4 * sz.bop_entries, 16)]
+    nscratch = int(ed.LIB.df11_encode_device_scratch_bytes(n))
+    scratch = torch.empty(nscratch, dtype=torch.uint8, device=dev)
+    out = ed.df11_device_encode(*[b.data_ptr() for b in bufs], scratch.data_ptr(), nscratch)
+    cnt = torch.empty(256, dtype=torch.int64, device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def hist():
+        ed._check("df11_histogram_device", ed.LIB.df11_histogram_device(
+            ed.FORMATS[fmt], ctypes.c_void_p(w.data_ptr()), n, ctypes.c_void_p(cnt.data_ptr()), sh))
+
+    def enc():
+        ed._check("df11_encode_device", ed.LIB.df11_encode_device(
+            ed.FORMATS[fmt], ctypes.byref(cb), ctypes.c_void_p(w.data_ptr()), n, args.tile_windows,
+            8, ctypes.byref(sz), ctypes.byref(out), sh))
+
+    for _ in range(max(1, min(args.warmup, 10))):
+        hist()
+        enc()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for a, b, c in ev:
+        a.record(stream)
+        hist()
+        b.record(stream)
+        enc()
+        c.record(stream)
+    torch.cuda.synchronize()
+    h_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    e_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    t0 = time.perf_counter()
+    hcb = ed.df11_build_codebook(tensors, fmt)
+    hs = ed.df11_encode(hcb, tensors, args.tile_windows, 8, fmt)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    exact = (np.array_equal(bufs[0].cpu().numpy(), hs.stream)
+             and np.array_equal(bufs[1].cpu().numpy(), hs.sm)
+             and np.array_equal(bufs[2].cpu().numpy()[: hs.gaps.size], hs.gaps)
+             and np.array_equal(bufs[3].cpu().numpy().view(np.uint32), hs.block_out_pos)
+             and int(bufs[4][:4].cpu().numpy().view(np.uint32)[0]) == hs.max_tile_symbols)
+    total_ms = float(h_ms.mean() + e_ms.mean())
+    in_bytes = n * (2 if fmt == "bf16" else 1)
+    line = {
+        "metric": "GPU encode GB/s (input weights)", "value": round(in_bytes / (total_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "higher_is_better": True,
+        "dtype": "u32", "data": "synthetic",
+        "config": {"workload": cfg.name if fmt == "bf16" else f"{cfg.name}_{fmt}", "n_weights": n,
+                   "layout": f"T{args.tile_windows}xB8", "byte_exact_vs_host_encoder": bool(exact)},
+        "device_ms": {"histogram": round(float(h_ms.mean()), 4), "encode": round(float(e_ms.mean()), 4),
+                      "codebook_on_host": round(codebook_ms, 3)},
+        "host_encoder_ms": round(host_ms, 1),
     }
     print(json.dumps(line), flush=True)
     if not exact:

@@ -124,6 +124,18 @@ class df11_gemv_tensor(ctypes.Structure):
     ]
 
 
+class df11_device_encode(ctypes.Structure):
+    _fields_ = [
+        ("stream", ctypes.c_void_p),
+        ("sm", ctypes.c_void_p),
+        ("gaps", ctypes.c_void_p),
+        ("block_out_pos", ctypes.c_void_p),
+        ("d_max_tile_symbols", ctypes.c_void_p),
+        ("scratch", ctypes.c_void_p),
+        ("scratch_bytes", ctypes.c_uint64),
+    ]
+
+
 DF11_PIPELINE_MAX_SLOTS = 4
 # df11_format; the names are what the binding's ``fmt`` arguments accept
 FORMATS = {"bf16": 0, "fp8_e4m3": 1, "fp8_e5m2": 2}
@@ -168,11 +180,23 @@ def _load():
     L.df11_pipeline_acquire.argtypes = [vp, ctypes.c_uint32, vp]
     L.df11_pipeline_release.argtypes = [vp, ctypes.c_uint32, vp]
     L.df11_gemv_bf16.argtypes = [vp, ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32, vp, vp, vp]
+    L.df11_build_codebook_from_counts.argtypes = [_u64p, ctypes.POINTER(df11_codebook)]
+    L.df11_encode_size_from_counts.argtypes = [ctypes.c_uint32, ctypes.POINTER(df11_codebook),
+                                               _u64p, ctypes.c_uint64, ctypes.c_uint32,
+                                               ctypes.c_uint32, ctypes.POINTER(df11_sizes)]
+    L.df11_histogram_device.argtypes = [ctypes.c_uint32, vp, ctypes.c_uint64, vp, vp]
+    L.df11_encode_device_scratch_bytes.argtypes = [ctypes.c_uint64]
+    L.df11_encode_device_scratch_bytes.restype = ctypes.c_uint64
+    L.df11_encode_device.argtypes = [ctypes.c_uint32, ctypes.POINTER(df11_codebook), vp,
+                                     ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                     ctypes.POINTER(df11_sizes), ctypes.POINTER(df11_device_encode),
+                                     vp]
     for f in (L.df11_build_codebook, L.df11_encode_size, L.df11_encode,
               L.df11_build_codebook_fmt, L.df11_encode_size_fmt, L.df11_encode_fmt,
               L.df11_decompress_block, L.df11_decompress_tensor, L.df11_pipeline_create,
               L.df11_pipeline_destroy, L.df11_pipeline_decompress, L.df11_pipeline_acquire,
-              L.df11_pipeline_release, L.df11_gemv_bf16):
+              L.df11_pipeline_release, L.df11_gemv_bf16, L.df11_build_codebook_from_counts,
+              L.df11_encode_size_from_counts, L.df11_histogram_device, L.df11_encode_device):
         f.restype = ctypes.c_int
     return L
 
@@ -320,9 +344,11 @@ class DeviceStream:
 
     Holds the ctypes descriptor passed to df11_decompress_*; the host-side
     tensor metadata (offsets, tile ranges) stays in numpy arrays it owns.
+    Built from a HostStream (uploaded) or, by encode_on_device, from arrays
+    written on the device.
     """
 
-    def __init__(self, hs: HostStream, cb: df11_codebook, device="cuda"):
+    def __init__(self, hs: HostStream, cb: df11_codebook, device="cuda", arrays=None):
         import torch
 
         def up(a):
@@ -330,10 +356,13 @@ class DeviceStream:
             return t.to(device)
 
         self.host = hs
-        self.stream = up(hs.stream)
-        self.sm = up(hs.sm)
-        self.gaps = up(hs.gaps if hs.gaps.size else np.zeros(1, np.uint8))
-        self.block_out_pos = up(hs.block_out_pos)
+        if arrays is None:
+            self.stream = up(hs.stream)
+            self.sm = up(hs.sm)
+            self.gaps = up(hs.gaps if hs.gaps.size else np.zeros(1, np.uint8))
+            self.block_out_pos = up(hs.block_out_pos)
+        else:
+            self.stream, self.sm, self.gaps, self.block_out_pos = arrays
         self.tables = up(table_image(cb))
         self.tensor_offsets = np.ascontiguousarray(hs.tensor_offsets, dtype=np.uint64)
         self.tensor_tiles = np.ascontiguousarray(
@@ -471,6 +500,97 @@ def df11_gemv_bf16(w, layout, x, y, stream=None) -> None:
     _check("df11_gemv_bf16",
            LIB.df11_gemv_bf16(ctypes.c_void_p(w.data_ptr()), arr, n, ctypes.c_void_p(x.data_ptr()),
                               ctypes.c_void_p(y.data_ptr()), _stream_handle(stream)))
+
+
+# ---------------------------------------------------------------- device encoder
+
+
+def df11_histogram_device(w, fmt: str = "bf16", stream=None):
+    """Exponent histogram of the device tensor ``w`` (uint64[256] on its device)."""
+    import torch
+
+    counts = torch.empty(256, dtype=torch.int64, device=w.device)
+    _check("df11_histogram_device",
+           LIB.df11_histogram_device(_format(fmt), ctypes.c_void_p(w.data_ptr()), w.numel(),
+                                     ctypes.c_void_p(counts.data_ptr()), _stream_handle(stream)))
+    return counts
+
+
+def df11_build_codebook_from_counts(counts) -> df11_codebook:
+    c = np.ascontiguousarray(np.asarray(counts), dtype=np.uint64)
+    cb = df11_codebook()
+    _check("df11_build_codebook_from_counts",
+           LIB.df11_build_codebook_from_counts(c.ctypes.data_as(_u64p), ctypes.byref(cb)))
+    return cb
+
+
+def encode_on_device(tensors, fmt: str = "bf16", tile_windows: int = DEFAULT_TILE_WINDOWS,
+                     window_bytes: int = DEFAULT_WINDOW_BYTES, stream=None):
+    """Compress device tensors (16-bit for BF16, 8-bit for FP8) into a
+    DeviceStream without moving the weights to the host: per-tensor device
+    histograms, the codebook built on the host from them, then
+    df11_encode_device on the concatenated unit.  Returns (DeviceStream, codebook)."""
+    import torch
+
+    size = 2 if fmt == "bf16" else 1
+    flat = []
+    for t in tensors:
+        if t.element_size() != size:
+            raise TypeError(f"{fmt} tensors must have {8 * size}-bit elements")
+        flat.append(t.reshape(-1).view(torch.int16 if size == 2 else torch.uint8))
+    unit = torch.cat(flat) if len(flat) != 1 else flat[0].contiguous()
+    n = unit.numel()
+    per = [df11_histogram_device(t.contiguous(), fmt, stream) for t in flat]
+    per_h = [c.cpu().numpy().view(np.uint64) for c in per]
+    counts = np.sum(per_h, axis=0).astype(np.uint64) if per_h else np.zeros(256, np.uint64)
+    cb = df11_build_codebook_from_counts(counts)
+    sz = df11_sizes()
+    _check("df11_encode_size_from_counts",
+           LIB.df11_encode_size_from_counts(_format(fmt), ctypes.byref(cb),
+                                            counts.ctypes.data_as(_u64p), n, tile_windows,
+                                            window_bytes, ctypes.byref(sz)))
+    dev = unit.device
+    st = torch.empty(sz.stream_bytes, dtype=torch.uint8, device=dev)
+    sm = torch.empty(sz.sm_bytes, dtype=torch.uint8, device=dev)
+    gaps = torch.empty(max(16, sz.n_windows), dtype=torch.uint8, device=dev)
+    bop = torch.empty(sz.bop_entries, dtype=torch.int32, device=dev)
+    mx = torch.empty(4, dtype=torch.int32, device=dev)
+    nbytes = int(LIB.df11_encode_device_scratch_bytes(n))
+    scratch = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    sp = scratch.data_ptr()
+    out = df11_device_encode(st.data_ptr(), sm.data_ptr(), gaps.data_ptr(), bop.data_ptr(),
+                             mx.data_ptr(), (sp + 255) // 256 * 256, nbytes)
+    _check("df11_encode_device",
+           LIB.df11_encode_device(_format(fmt), ctypes.byref(cb), ctypes.c_void_p(unit.data_ptr()),
+                                  n, tile_windows, window_bytes, ctypes.byref(sz),
+                                  ctypes.byref(out), _stream_handle(stream)))
+    # per-tensor offsets and tile ranges, as df11_encode computes them
+    lens = np.ctypeslib.as_array(cb.code_len).astype(np.uint64)
+    tshift = (8 * window_bytes * tile_windows).bit_length() - 1  # log2 of tile bits
+    offs = np.zeros(len(flat) + 1, dtype=np.uint64)
+    tiles = np.zeros(max(2, 2 * len(flat)), dtype=np.uint64)
+    g = bit = 0
+    for k, (t, c) in enumerate(zip(flat, per_h)):
+        offs[k] = g
+        bits_k = int((c * lens).sum())
+        tiles[2 * k] = bit >> tshift
+        if t.numel():
+            last = int(t[-1].item()) & (0xFFFF if size == 2 else 0xFF)
+            sym = (last >> 7) & 0xFF if fmt == "bf16" else \
+                ((last >> 3) & 0xF if fmt == "fp8_e4m3" else (last >> 2) & 0x1F)
+            tiles[2 * k + 1] = ((bit + bits_k - int(lens[sym])) >> tshift) + 1
+        else:
+            tiles[2 * k + 1] = tiles[2 * k]
+        g += t.numel()
+        bit += bits_k
+    offs[len(flat)] = n
+    torch.cuda.synchronize(dev)
+    hs = HostStream(np.zeros(0, np.uint8), np.zeros(0, np.uint8), np.zeros(sz.n_windows, np.uint8),
+                    np.zeros(sz.bop_entries, np.uint32), offs, tiles[: 2 * len(flat)],
+                    tile_windows, window_bytes, int(mx[0].item()), n, int(sz.total_bits),
+                    int(sz.n_tiles), _format(fmt))
+    ds = DeviceStream(hs, cb, dev, arrays=(st, sm, gaps, bop))
+    return ds, cb
 
 
 def table_bytes(cb: df11_codebook) -> int:

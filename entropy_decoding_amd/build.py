@@ -36,12 +36,15 @@ def build_library(verbose: bool = False, extra_hip_flags=()) -> str:
           "-o", host_o], verbose)
     _run([HIPCC, *HIP_FLAGS, *extra_hip_flags, "-I", INCLUDE, "-c",
           os.path.join(CSRC, "df11_device.hip"), "-o", dev_o], verbose)
-    pipe_o = os.path.join(BUILD, "df11_pipeline.o")
-    _run([HIPCC, *HIP_FLAGS, *extra_hip_flags, "-I", INCLUDE, "-c",
-          os.path.join(CSRC, "df11_pipeline.hip"), "-o", pipe_o], verbose)
+    objs = [host_o, dev_o]
+    for name in ("df11_pipeline", "df11_encode_device"):
+        o = os.path.join(BUILD, name + ".o")
+        _run([HIPCC, *HIP_FLAGS, *extra_hip_flags, "-I", INCLUDE, "-c",
+              os.path.join(CSRC, name + ".hip"), "-o", o], verbose)
+        objs.append(o)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", host_o, dev_o, pipe_o,
-          "-pthread", "-o", tmp], verbose)
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-pthread", "-o", tmp],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

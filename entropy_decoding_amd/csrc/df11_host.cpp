@@ -496,6 +496,15 @@ int df11_build_codebook_fmt(uint32_t format, const void *const *tensors, const u
         std::vector<uint64_t> per;
         uint64_t counts[kSyms];
         histogram_any(format, pieces, per, counts);
+        return df11_build_codebook_from_counts(counts, cb);
+    } catch (...) {
+        return DF11_E_INVALID;
+    }
+}
+
+int df11_build_codebook_from_counts(const uint64_t *counts, df11_codebook *cb) {
+    try {
+        if (!counts || !cb) return DF11_E_INVALID;
         uint64_t n = 0;
         for (int s = 0; s < kSyms; s++) n += counts[s];
         if (n == 0) return DF11_E_INVALID;
@@ -511,6 +520,18 @@ int df11_build_codebook_fmt(uint32_t format, const void *const *tensors, const u
     } catch (...) {
         return DF11_E_INVALID;
     }
+}
+
+int df11_encode_size_from_counts(uint32_t format, const df11_codebook *cb, const uint64_t *counts,
+                                 uint64_t n_weights, uint32_t tile_windows, uint32_t window_bytes,
+                                 df11_sizes *out) {
+    if (!cb || !counts || !out || !valid_layout(tile_windows, window_bytes) ||
+        !valid_codebook(cb) || !valid_format_layout(format, tile_windows))
+        return DF11_E_INVALID;
+    uint64_t n = 0;
+    for (int s = 0; s < kSyms; s++) n += counts[s];
+    if (n != n_weights) return DF11_E_INVALID;
+    return sizes_from_counts(format, cb, counts, n, tile_windows, window_bytes, out);
 }
 
 int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n_tensors,

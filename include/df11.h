@@ -245,6 +245,17 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors,
                 const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
                 uint32_t window_bytes, df11_host_stream *out);
 
+/* The codebook of df11_build_codebook from an exponent histogram counts[256]
+ * (e.g. from df11_histogram_device).  Errors: DF11_E_INVALID (null, all zero),
+ * DF11_E_LUT_BUDGET. */
+int df11_build_codebook_from_counts(const uint64_t *counts, df11_codebook *cb);
+
+/* df11_encode_size from a histogram of n_weights weights (the counts must sum
+ * to n_weights).  Errors: DF11_E_INVALID, DF11_E_SYMBOL. */
+int df11_encode_size_from_counts(uint32_t format, const df11_codebook *cb, const uint64_t *counts,
+                                 uint64_t n_weights, uint32_t tile_windows, uint32_t window_bytes,
+                                 df11_sizes *out);
+
 /* df11_encode for any df11_format (FP8 requires T = 64); out->format is set. */
 int df11_encode_fmt(uint32_t format, const df11_codebook *cb, const void *const *tensors,
                     const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,
@@ -279,6 +290,50 @@ int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, void *out,
 
 /* Static description of a status code. */
 const char *df11_status_string(int status);
+
+/*
+ * GPU-side encoder -- for weights already in device memory (a fine-tuned or
+ * freshly quantized model): the histogram runs on the device, the codebook is
+ * built on the host from it (df11_build_codebook_from_counts), and the
+ * encoding runs on the device and writes exactly the bytes df11_encode would
+ * (frequency-chosen codes for the exponents, DFloat11 abstract).  One unit is
+ * one contiguous device array of n weights (concatenate a block's tensors
+ * first); per-tensor offsets and tile ranges follow from per-tensor
+ * histograms as in df11_encode.
+ */
+
+/* counts[s] = number of weights with exponent symbol s, into d_counts
+ * (device, 256 uint64, 16-byte aligned; cleared by the call).  w: device,
+ * 16-byte aligned.  Asynchronous on stream st. */
+int df11_histogram_device(uint32_t format, const void *w, uint64_t n, uint64_t *d_counts,
+                          df11_hip_stream st);
+
+/* Device scratch df11_encode_device needs for n weights (per-4096-weight bit
+ * totals and start bits). */
+uint64_t df11_encode_device_scratch_bytes(uint64_t n_weights);
+
+/* Device buffers of df11_encode_device (all device memory, 16-byte aligned;
+ * scratch 256-byte aligned).  Sizes: those of df11_sizes for the stream, sm,
+ * gaps and block_out_pos arrays; d_max_tile_symbols: 16 bytes, of which the
+ * first uint32 receives max_tile_symbols. */
+typedef struct df11_device_encode {
+    uint8_t *stream;
+    uint8_t *sm;
+    uint8_t *gaps;
+    uint32_t *block_out_pos;
+    uint32_t *d_max_tile_symbols;
+    void *scratch;
+    uint64_t scratch_bytes;
+} df11_device_encode;
+
+/* Encodes the n weights at w (device) with codebook cb under layout (T, B)
+ * into out; sz must be df11_encode_size_from_counts's result for the same
+ * weights.  Asynchronous on stream st (the buffers are complete when the
+ * stream reaches that point).  Errors: DF11_E_INVALID (null, misaligned or
+ * inconsistent arguments, n == 0), DF11_E_HIP. */
+int df11_encode_device(uint32_t format, const df11_codebook *cb, const void *w, uint64_t n,
+                       uint32_t tile_windows, uint32_t window_bytes, const df11_sizes *sz,
+                       const df11_device_encode *out, df11_hip_stream st);
 
 /*
  * Overlapped block pipeline -- device orchestration.  Decompression is done
