@@ -11,6 +11,7 @@ and the CPU oracle's bit-serial decode timed on this host as a baseline.
 
   python bench.py [--steps K] [--warmup W] [--config 2|1|0|3a|3b|3c|4] [--tile-windows 64|256|512]
   python bench.py --pipeline     # 8B model blocks, next block decompressed while a GEMV reads this one
+  python bench.py --fused        # y = W x straight from the compressed block vs decompress + GEMV
 """
 
 from __future__ import annotations
@@ -194,6 +195,9 @@ def main():
     ap.add_argument("--pipeline", action="store_true",
                     help="time the overlapped block pipeline with a GEMV consumer over the "
                          "32 blocks of the 8B model instead")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the fused decode + GEMV on the workload's block against "
+                         "decompression followed by a GEMV, and a GEMV on resident BF16")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decoder needs no cross-GPU exchange (each GPU "
@@ -213,6 +217,8 @@ def main():
         return pipeline_bench(args, torch, ed, sw)
     if args.encode:
         return encode_bench(args, torch, ed, sw)
+    if args.fused:
+        return fused_bench(args, torch, ed, sw)
     if args.format != "bf16" and (args.tile_windows != 64 or args.config in ("4",)):
         print("FP8 workloads use 64-window tiles and single-unit configs", file=sys.stderr)
         sys.exit(2)
@@ -596,6 +602,118 @@ def pipeline_bench(args, torch, ed, sw):
     }
     print(json.dumps(line), flush=True)
     if not exact:
+        sys.exit(1)
+
+
+def fused_bench(args, torch, ed, sw):
+    """One block's matrix-vector products y = W x (fp32 x and y) three ways:
+    the fused kernel reading only the compressed block (df11_decompress_gemv),
+    decompression to BF16 followed by the GEMV (two launches), and the GEMV on
+    resident BF16 weights.  Times are HIP events on the launch stream; caches
+    are evicted between steps when the block fits in them."""
+    import oracle
+
+    if args.format != "bf16" or args.tile_windows != 64:
+        print("the fused GEMV takes BF16 units with 64-window tiles", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    cfg = sw.config(args.config)
+    unit = cfg.units[0]
+    shapes = [shape for _, shape in unit.tensors]
+    tensors = sw.gen_unit(unit)
+    cb = ed.df11_build_codebook(tensors)
+    hs = ed.df11_encode(cb, tensors, 64, 8)
+    ds = ed.DeviceStream(hs, cb, dev)
+    n = hs.n_weights
+    layout = ed.gemv_layout(shapes)
+    rng = np.random.default_rng(5)
+    xh = rng.standard_normal(layout[2]).astype(np.float32)
+    x = torch.from_numpy(xh).to(dev)
+    y_f = torch.zeros(layout[3], dtype=torch.float32, device=dev)
+    y_s = torch.zeros_like(y_f)
+    y_r = torch.zeros_like(y_f)
+    w_res = torch.from_numpy(np.concatenate(tensors).view(np.int16)).to(dev)
+    buf = torch.empty(n, dtype=torch.int16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    scratch = torch.empty(int(ed.LIB.df11_decompress_gemv_scratch_bytes(ed.ctypes.byref(ds.desc))),
+                          dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    dec_bytes = algorithmic_bytes(hs, cb)
+    read_bytes = dec_bytes - 2 * n
+    vec_bytes = 4 * (layout[2] + layout[3])
+    small = dec_bytes < (1 << 30)
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if small else None
+    sink = torch.zeros((), dtype=torch.int32, device=dev)
+
+    def fused():
+        ed.df11_decompress_gemv(ds, layout, x, y_f, scratch, status, stream)
+
+    def sequential():
+        ed.df11_decompress_block(ds, buf, status, stream)
+        ed.df11_gemv_bf16(buf, layout, x, y_s, stream)
+
+    def resident():
+        ed.df11_gemv_bf16(w_res, layout, x, y_r, stream)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            if flush is not None:
+                torch.amax(flush, dim=0, out=sink)
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    res = {name: timed(fn) for name, fn in
+           (("fused", fused), ("decompress_then_gemv", sequential), ("bf16_gemv", resident))}
+    ok = int(status.item()) == 0 and torch.equal(buf, w_res)
+    # sampled rows of every matrix against the oracle's float64 product, within
+    # the rounding bound of each kernel's summation order
+    yf, ys = y_f.cpu().numpy().astype(np.float64), y_s.cpu().numpy().astype(np.float64)
+    bop = hs.block_out_pos.astype(np.int64)
+    per_lane = -(-(int(hs.max_tile_symbols) // 8 + 2) // 64)
+    u = 2.0 ** -24
+    off = xo = yo = 0
+    for (rows, cols), w in zip(shapes, tensors):
+        r = np.unique(np.linspace(0, rows - 1, 64).astype(np.int64))
+        W = w.reshape(rows, cols)[r].reshape(-1)
+        ref = oracle.gemv(W, [(r.size, cols)], xh[xo:xo + cols])
+        absum = np.abs(oracle.bf16_to_f64(W)).reshape(r.size, cols) @ np.abs(xh[xo:xo + cols])
+        starts = off + r * cols
+        tiles = (np.searchsorted(bop, starts + cols - 1, side="right")
+                 - np.searchsorted(bop, starts, side="right") + 1)
+        df = 8 + per_lane + 6 + tiles
+        ds_ = -(-cols // 64) + 6
+        ok &= bool(np.all(np.abs(yf[yo + r] - ref) <= df * u / (1 - df * u) * absum + 1e-30))
+        ok &= bool(np.all(np.abs(ys[yo + r] - ref) <= ds_ * u / (1 - ds_ * u) * absum + 1e-30))
+        off += rows * cols
+        xo += cols
+        yo += rows
+    f = res["fused"]
+    achieved = (read_bytes + vec_bytes) / (f.mean() * 1e-3) / 1e9
+    line = {
+        "metric": "fused decompress+GEMV time per block",
+        "value": round(float(f.mean()), 4), "unit": "ms per block", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+        "vs_baseline": None, "dtype": "u32+f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "n_weights": n, "layout": "T64xB8",
+                   "within_rounding_bound": bool(ok), "caches_flushed_between_steps": small},
+        "ms": {k: {"mean": round(float(v.mean()), 4), "p50": round(float(np.percentile(v, 50)), 4)}
+               for k, v in res.items()},
+        "speedup_vs_decompress_then_gemv": round(float(res["decompress_then_gemv"].mean() / f.mean()), 3),
+        "speedup_vs_bf16_gemv": round(float(res["bf16_gemv"].mean() / f.mean()), 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": read_bytes + vec_bytes},
+    }
+    print(json.dumps(line), flush=True)
+    if not ok:
         sys.exit(1)
 
 

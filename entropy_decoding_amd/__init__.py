@@ -181,6 +181,11 @@ def _load():
     L.df11_pipeline_release.argtypes = [vp, ctypes.c_uint32, vp]
     L.df11_gemv_bf16.argtypes = [vp, ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32, vp, vp, vp]
     L.df11_build_codebook_from_counts.argtypes = [_u64p, ctypes.POINTER(df11_codebook)]
+    L.df11_decompress_gemv_scratch_bytes.argtypes = [ctypes.POINTER(df11_device_stream)]
+    L.df11_decompress_gemv_scratch_bytes.restype = ctypes.c_uint64
+    L.df11_decompress_gemv.argtypes = [ctypes.POINTER(df11_device_stream),
+                                       ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32, vp, vp,
+                                       vp, ctypes.c_uint64, vp, vp]
     L.df11_encode_size_from_counts.argtypes = [ctypes.c_uint32, ctypes.POINTER(df11_codebook),
                                                _u64p, ctypes.c_uint64, ctypes.c_uint32,
                                                ctypes.c_uint32, ctypes.POINTER(df11_sizes)]
@@ -196,7 +201,8 @@ def _load():
               L.df11_decompress_block, L.df11_decompress_tensor, L.df11_pipeline_create,
               L.df11_pipeline_destroy, L.df11_pipeline_decompress, L.df11_pipeline_acquire,
               L.df11_pipeline_release, L.df11_gemv_bf16, L.df11_build_codebook_from_counts,
-              L.df11_encode_size_from_counts, L.df11_histogram_device, L.df11_encode_device):
+              L.df11_encode_size_from_counts, L.df11_histogram_device, L.df11_encode_device,
+              L.df11_decompress_gemv):
         f.restype = ctypes.c_int
     return L
 
@@ -591,6 +597,28 @@ def encode_on_device(tensors, fmt: str = "bf16", tile_windows: int = DEFAULT_TIL
                     int(sz.n_tiles), _format(fmt))
     ds = DeviceStream(hs, cb, dev, arrays=(st, sm, gaps, bop))
     return ds, cb
+
+
+def df11_decompress_gemv(ds: DeviceStream, layout, x, y, scratch=None, status=None,
+                         stream=None) -> None:
+    """y = W x per matrix of ``layout`` (from gemv_layout, matching the unit's
+    tensors) computed straight from the compressed unit ``ds``.  ``scratch``: a
+    device uint8 tensor of df11_decompress_gemv_scratch_bytes bytes, allocated
+    here when not given."""
+    import torch
+
+    arr, n, nx, ny = layout
+    if x.dtype.itemsize != 4 or y.dtype.itemsize != 4 or x.numel() < nx or y.numel() < ny:
+        raise ValueError("x and y must be float32 device tensors covering the layout")
+    need = int(LIB.df11_decompress_gemv_scratch_bytes(ctypes.byref(ds.desc)))
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=x.device)
+    sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
+    _check("df11_decompress_gemv",
+           LIB.df11_decompress_gemv(ctypes.byref(ds.desc), arr, n, ctypes.c_void_p(x.data_ptr()),
+                                    ctypes.c_void_p(y.data_ptr()),
+                                    ctypes.c_void_p(scratch.data_ptr()), scratch.numel(), sp,
+                                    _stream_handle(stream)))
 
 
 def table_bytes(cb: df11_codebook) -> int:

@@ -578,8 +578,11 @@ __device__ __forceinline__ uint2 chunk_sm(const KArgs &a, const uint2 (&smv)[JP]
 // and last outputs are usually shared with the neighbouring tiles; they are
 // written element by element, one lane per element, in one pass.  FMT is the
 // weight format (BF16 or FP8): only the final assembly differs.
-template <int JP, int FMT>
-__global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
+//
+// Epi is what happens to a decoded tile: StoreEpi writes the weights, the
+// fused GEMV consumes them (df11_decompress_gemv).
+template <int JP, int FMT, class Epi>
+__device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi) {
     using F = OutFmt<FMT>;
     constexpr uint32_t CH = F::kChunk;
     __shared__ __align__(16) uint8_t fast[kLutOff];
@@ -658,6 +661,18 @@ __global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
+        epi.template tile<JP, FMT>(a, tile, P0, P1, A0, n8, smv, sm0, ebuf, lane);
+        cur = nxt;
+    }
+}
+
+struct StoreEpi {
+    template <int JP, int FMT>
+    __device__ __forceinline__ void tile(const KArgs &a, uint32_t, uint32_t P0, uint32_t P1,
+                                         uint32_t A0, uint32_t n8, const uint2 (&smv)[JP],
+                                         const uint8_t *sm0, const uint8_t *ebuf, uint32_t lane) {
+        using F = OutFmt<FMT>;
+        constexpr uint32_t CH = F::kChunk;
         // whole chunks: the lanes of the wave write 1 KiB contiguously per j
         const uint32_t lo = max(P0, a.out_lo), hi = min(P1, a.out_hi);
 #pragma unroll
@@ -683,8 +698,212 @@ __global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
                 if (!whole && i >= lo && i < hi) F::store1(a, i, lane < CH ? sh : sl, k, ebuf[CH * c + k]);
             }
         }
-        cur = nxt;
     }
+};
+
+template <int JP, int FMT>
+__global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
+    StoreEpi epi;
+    wave_tiles<JP, FMT>(a, epi);
+}
+
+// ---------------------------------------------------------------- fused GEMV
+//
+// y = W x for the matrices of a BF16 unit, straight from the compressed
+// stream: a decoded tile multiplies its weights by x instead of storing them.
+// A tile touches at most kRowsPerTile consecutive rows (the host checks this
+// from max_tile_symbols and the narrowest matrix); each lane accumulates its
+// chunks' products per row, a butterfly over the wave sums the lanes, and the
+// tile's row sums go to a scratch array; a second kernel adds, for every row,
+// the sums of the tiles that hold it, in tile order.  Every sum is formed in a
+// fixed order, so results are deterministic.
+
+constexpr uint32_t kRowsPerTile = 4;
+
+struct GemvDesc {
+    uint32_t n;
+    uint32_t off[DF11_GEMV_MAX_TENSORS + 1];   // first element of each matrix in the unit, then N
+    uint32_t row0[DF11_GEMV_MAX_TENSORS + 1];  // first global row of each matrix, then the total
+    uint32_t cols[DF11_GEMV_MAX_TENSORS];
+    uint32_t x_off[DF11_GEMV_MAX_TENSORS], y_off[DF11_GEMV_MAX_TENSORS];
+};
+
+// matrix holding unit element g
+__device__ __forceinline__ uint32_t matrix_of(const GemvDesc &g, uint32_t e) {
+    uint32_t k = 0;
+    while (k + 1 < g.n && e >= g.off[k + 1]) k++;
+    return k;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// fp32 value of a BF16 weight from its sign+mantissa byte and exponent byte
+__device__ __forceinline__ float bf16_value(uint32_t sm, uint32_t e) {
+    return __uint_as_float(((sm & 0x80u) << 24) | (e << 23) | ((sm & 0x7Fu) << 16));
+}
+
+struct GemvEpi {
+    const GemvDesc *g;
+    const float *x;
+    float *part;     // kRowsPerTile row sums per tile
+    uint32_t *row_a;  // first global row of each tile
+
+    template <int JP, int FMT>
+    __device__ __forceinline__ void tile(const KArgs &a, uint32_t tile, uint32_t P0, uint32_t P1,
+                                         uint32_t A0, uint32_t n8, const uint2 (&smv)[JP],
+                                         const uint8_t *sm0, const uint8_t *ebuf, uint32_t lane) {
+        const GemvDesc &d = *g;
+        if (P0 == P1) {  // a tile past the last code start holds no weights
+            if (lane < kRowsPerTile) part[uint64_t(tile) * kRowsPerTile + lane] = 0.0f;
+            if (lane == 0) row_a[tile] = 0;
+            return;
+        }
+        // the tile's first and last rows (uniform over the wave)
+        const uint32_t ka = matrix_of(d, P0), kb = matrix_of(d, P1 - 1);
+        const uint32_t ra = d.row0[ka] + (P0 - d.off[ka]) / d.cols[ka];
+        const uint32_t rb = d.row0[kb] + (P1 - 1 - d.off[kb]) / d.cols[kb];
+        if (rb - ra >= kRowsPerTile) {
+            // impossible for a valid unit (the host checks the widest tile
+            // against the narrowest matrix); a corrupt one is reported
+            if (lane < kRowsPerTile) part[uint64_t(tile) * kRowsPerTile + lane] = 0.0f;
+            if (lane == 0) {
+                row_a[tile] = ra;
+                if (a.status) atomicExch(a.status, int32_t(DF11_E_CORRUPT));
+            }
+            return;
+        }
+        float acc[kRowsPerTile] = {};
+        if (ka == kb) {
+            // rows ra .. ra+3 of one matrix start at rs, b1, b2, b3: a chunk's
+            // row and column follow from three comparisons
+            const uint32_t cols = d.cols[ka];
+            const uint32_t rs = d.off[ka] + (ra - d.row0[ka]) * cols;
+            const uint32_t b1 = rs + cols, b2 = b1 + cols, b3 = b2 + cols;
+            const float *xk = x + d.x_off[ka];
+            // one lane's chunks lie in non-decreasing rows: a running sum per
+            // lane, moved to its row's accumulator when the row changes
+            float run = 0.0f;
+            uint32_t cur = 0;
+            auto chunk = [&](uint32_t c, uint2 s8) {
+                const uint32_t gi = A0 + 8 * c;
+                const uint32_t idx = uint32_t(gi >= b1) + uint32_t(gi >= b2) + uint32_t(gi >= b3);
+                const uint32_t r0 = gi >= b3 ? b3 : gi >= b2 ? b2 : gi >= b1 ? b1 : rs;
+                if (idx != cur) {
+#pragma unroll
+                    for (uint32_t i = 0; i < kRowsPerTile; i++) acc[i] += cur == i ? run : 0.0f;
+                    run = 0.0f;
+                    cur = idx;
+                }
+                const float4 x0 = *reinterpret_cast<const float4 *>(xk + (gi - r0));
+                const float4 x1 = *reinterpret_cast<const float4 *>(xk + (gi - r0) + 4);
+                const uint2 e8 = *reinterpret_cast<const uint2 *>(ebuf + 8 * c);
+                uint32_t wv[4];
+                assemble4(s8.x, e8.x, wv[0], wv[1]);
+                assemble4(s8.y, e8.y, wv[2], wv[3]);
+                run = fmaf(__uint_as_float(wv[0] << 16), x0.x, run);
+                run = fmaf(__uint_as_float(wv[0] & 0xFFFF0000u), x0.y, run);
+                run = fmaf(__uint_as_float(wv[1] << 16), x0.z, run);
+                run = fmaf(__uint_as_float(wv[1] & 0xFFFF0000u), x0.w, run);
+                run = fmaf(__uint_as_float(wv[2] << 16), x1.x, run);
+                run = fmaf(__uint_as_float(wv[2] & 0xFFFF0000u), x1.y, run);
+                run = fmaf(__uint_as_float(wv[3] << 16), x1.z, run);
+                run = fmaf(__uint_as_float(wv[3] & 0xFFFF0000u), x1.w, run);
+            };
+            // whole chunks
+#pragma unroll
+            for (int j = 0; j < JP; j++) {
+                const uint32_t c = lane + j * 64;
+                const uint32_t gi = A0 + 8 * c;
+                if (c < n8 && gi >= P0 && gi + 8 <= P1) chunk(c, smv[j]);
+            }
+            for (uint32_t c = lane + JP * 64; c < n8; c += 64) {
+                const uint32_t gi = A0 + 8 * c;
+                if (gi >= P0 && gi + 8 <= P1) chunk(c, *reinterpret_cast<const uint2 *>(sm0 + 8 * c));
+            }
+#pragma unroll
+            for (uint32_t i = 0; i < kRowsPerTile; i++) acc[i] += cur == i ? run : 0.0f;
+            // the chunks holding P0 and P1-1 when they are not whole, one
+            // element per lane (lanes 0-7 and 8-15; once if they coincide)
+            const uint32_t ch = (P0 - A0) / 8, ct = (P1 - 1 - A0) / 8;
+            const uint2 sh = chunk_sm<JP, FMT>(a, smv, A0, ch), sl = chunk_sm<JP, FMT>(a, smv, A0, ct);
+            if (lane < 16 && (lane < 8 || ct != ch)) {
+                const uint32_t c = lane < 8 ? ch : ct, k = lane & 7u;
+                const uint32_t gi = A0 + 8 * c, i = gi + k;
+                const bool whole = gi >= P0 && gi + 8 <= P1;
+                if (!whole && i >= P0 && i < P1) {
+                    const uint2 s8 = lane < 8 ? sh : sl;
+                    const uint32_t sb = ((k < 4 ? s8.x : s8.y) >> (8 * (k & 3u))) & 0xFFu;
+                    const float w = bf16_value(sb, ebuf[8 * c + k]);
+                    const uint32_t idx = uint32_t(i >= b1) + uint32_t(i >= b2) + uint32_t(i >= b3);
+                    const uint32_t r0 = i >= b3 ? b3 : i >= b2 ? b2 : i >= b1 ? b1 : rs;
+                    const float xv = xk[i - r0];
+#pragma unroll
+                    for (uint32_t q = 0; q < kRowsPerTile; q++)
+                        if (idx == q) acc[q] = fmaf(w, xv, acc[q]);
+                }
+            }
+        } else {
+            // a tile that spans matrices (at most one per matrix boundary):
+            // element by element
+            for (uint32_t i = P0 + lane; i < P1; i += 64) {
+                const uint32_t k = matrix_of(d, i);
+                const uint32_t rel = i - d.off[k];
+                const uint32_t idx = d.row0[k] + rel / d.cols[k] - ra;
+                const float w = bf16_value(a.sm[i], ebuf[i - A0]);
+                const float xv = x[d.x_off[k] + rel % d.cols[k]];
+#pragma unroll
+                for (uint32_t q = 0; q < kRowsPerTile; q++)
+                    if (idx == q) acc[q] = fmaf(w, xv, acc[q]);
+            }
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < kRowsPerTile; i++) {
+            const float s = wave_sum_f(acc[i]);
+            if (lane == 0) part[uint64_t(tile) * kRowsPerTile + i] = s;
+        }
+        if (lane == 0) row_a[tile] = ra;
+    }
+};
+
+__global__ __launch_bounds__(kThreads) void df11_decode_gemv(KArgs a, GemvDesc d, const float *x,
+                                                             float *part, uint32_t *row_a) {
+    GemvEpi epi{&d, x, part, row_a};
+    wave_tiles<4, DF11_FORMAT_BF16>(a, epi);
+}
+
+// y for every row: the sums of the tiles that hold it, in tile order.
+__global__ __launch_bounds__(kThreads) void df11_gemv_rows(GemvDesc d, const uint32_t *bop,
+                                                           uint32_t n_tiles, const float *part,
+                                                           const uint32_t *row_a, float *y) {
+    const uint32_t r = blockIdx.x * kThreads + threadIdx.x;
+    if (r >= d.row0[d.n]) return;
+    uint32_t k = 0;
+    while (k + 1 < d.n && r >= d.row0[k + 1]) k++;
+    const uint32_t rs = d.off[k] + (r - d.row0[k]) * d.cols[k], re = rs + d.cols[k] - 1;
+    // the tiles holding elements rs and re: largest t with bop[t] <= element
+    auto tile_of = [&](uint32_t e) {
+        uint32_t lo = 0, hi = n_tiles;  // bop[lo] <= e < bop[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (bop[mid] <= e) lo = mid;
+            else hi = mid;
+        }
+        return lo;
+    };
+    const uint32_t t0 = tile_of(rs), t1 = tile_of(re);
+    float s = 0.0f;
+    // row_a of a tile skipped as corrupt was never written: the index is
+    // checked so that such a unit yields wrong sums (and its status), never
+    // a read outside part
+    for (uint32_t t = t0; t <= t1; t++) {
+        const uint32_t i = r - row_a[t];
+        if (i < kRowsPerTile) s += part[uint64_t(t) * kRowsPerTile + i];
+    }
+    y[d.y_off[k] + (r - d.row0[k])] = s;
 }
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
@@ -809,6 +1028,80 @@ int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, void *out,
     a.out_hi = uint32_t(end);
     a.out_shift = uint32_t(off);
     return launch(s, a, uint32_t(t1 - t0), static_cast<hipStream_t>(st));
+}
+
+uint64_t df11_decompress_gemv_scratch_bytes(const df11_device_stream *s) {
+    return s ? s->n_tiles * (4u * kRowsPerTile + 4u) + 256u : 0u;
+}
+
+int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t, uint32_t n_tensors,
+                         const float *x, float *y, void *scratch, uint64_t scratch_bytes,
+                         int32_t *d_status, df11_hip_stream st) {
+    KArgs a{};
+    int rc = prepare(s, a);
+    if (rc != DF11_OK) return rc;
+    if (s->format != DF11_FORMAT_BF16 || s->tile_windows != 64 || s->n_weights == 0 || !t ||
+        n_tensors == 0 || n_tensors > DF11_GEMV_MAX_TENSORS || !x || !y || !aligned(x, 16) ||
+        !scratch || !aligned(scratch, 16) || scratch_bytes < df11_decompress_gemv_scratch_bytes(s))
+        return DF11_E_INVALID;
+    GemvDesc d{};
+    d.n = n_tensors;
+    uint64_t off = 0, row = 0;
+    uint32_t min_cols = ~0u;
+    for (uint32_t k = 0; k < n_tensors; k++) {
+        // the matrices must tile the unit in order, with rows of whole 8-element chunks
+        if (t[k].w_offset != off || t[k].cols == 0 || t[k].cols % 8 || t[k].x_offset % 4 ||
+            t[k].rows == 0)
+            return DF11_E_INVALID;
+        d.off[k] = uint32_t(off);
+        d.row0[k] = uint32_t(row);
+        d.cols[k] = t[k].cols;
+        d.x_off[k] = uint32_t(t[k].x_offset);
+        d.y_off[k] = uint32_t(t[k].y_offset);
+        if (t[k].x_offset >= (uint64_t(1) << 32) || t[k].y_offset >= (uint64_t(1) << 32))
+            return DF11_E_INVALID;
+        off += uint64_t(t[k].rows) * t[k].cols;
+        row += t[k].rows;
+        min_cols = std::min(min_cols, t[k].cols);
+    }
+    if (off != s->n_weights || row >= (uint64_t(1) << 32)) return DF11_E_INVALID;
+    d.off[n_tensors] = uint32_t(off);
+    d.row0[n_tensors] = uint32_t(row);
+    // a tile of M outputs touches at most (M - 1) / min_cols + 2 rows
+    if (s->max_tile_symbols > 0 && (s->max_tile_symbols - 1) / min_cols + 2 > kRowsPerTile)
+        return DF11_E_INVALID;
+    float *part = static_cast<float *>(scratch);
+    uint32_t *row_a = reinterpret_cast<uint32_t *>(part + s->n_tiles * kRowsPerTile);
+    a.status = d_status;
+    a.out_lo = 0;
+    a.out_hi = uint32_t(s->n_weights);
+    a.n_tiles = uint32_t(s->n_tiles);
+    hipStream_t hs = static_cast<hipStream_t>(st);
+    // the launch shape of the 64-window kernel (see launch())
+    const size_t lds = size_t(a.ebuf_off) + size_t(a.exp_cap) * 4;
+    const void *fn = reinterpret_cast<const void *>(&df11_decode_gemv);
+    if (lds > 65536 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+        return DF11_E_INVALID;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess)
+        return DF11_E_HIP;
+    if (per_cu < 1) return DF11_E_INVALID;
+    const uint64_t slots = (s->n_tiles + 3) / 4;
+    const uint64_t want = std::max<uint64_t>(uint64_t(cus) * per_cu,
+                                             (slots + kTilesPerWorkgroup - 1) / kTilesPerWorkgroup);
+    const uint64_t used = std::min<uint64_t>(slots, want);
+    const uint32_t grid = uint32_t((used + kXcdBlock - 1) / kXcdBlock * kXcdBlock);
+    const float *xp = x;
+    void *args[] = {&a, &d, &xp, &part, &row_a};
+    if (hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, lds, hs) != hipSuccess)
+        return DF11_E_HIP;
+    const uint32_t rows = uint32_t(row);
+    hipLaunchKernelGGL(df11_gemv_rows, dim3((rows + kThreads - 1) / kThreads), dim3(kThreads), 0, hs,
+                       d, s->block_out_pos, uint32_t(s->n_tiles), part, row_a, y);
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
 }
 
 }  // extern "C"

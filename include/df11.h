@@ -405,6 +405,29 @@ typedef struct df11_gemv_tensor {
 int df11_gemv_bf16(const uint16_t *w, const df11_gemv_tensor *tensors, uint32_t n_tensors,
                    const float *x, float *y, df11_hip_stream st);
 
+/*
+ * df11_decompress_gemv -- device, decode fused into its consumer: the same
+ * products as df11_gemv_bf16 (y[y_offset_k + r] = sum over c of W_k[r][c] *
+ * x[x_offset_k + c], float32), computed straight from the compressed unit s
+ * without writing its BF16 weights, so HBM carries only the compressed bytes.
+ * A step toward decoding into the consumer's tiles (DFloat11 decompresses
+ * "online" right before use, abstract).  Requirements (DF11_E_INVALID
+ * otherwise): a BF16 unit with 64-window tiles; the tensors tile the unit in
+ * order (w_offset_k = sum of the previous rows * cols), cols_k multiples of 8,
+ * x 16-byte aligned with x_offset_k multiples of 4; no tile may touch more
+ * than 4 rows, i.e. (max_tile_symbols - 1) / min_k cols_k + 2 <= 4.  Each
+ * output is a sum formed in a fixed order: per weight chunk of 8 a chain of
+ * fused multiply-adds, per lane the chunks in order, a butterfly over the
+ * wave, then per row the tiles in order (deterministic; it differs from
+ * df11_gemv_bf16's order).  scratch: device, 16-byte aligned, at least
+ * df11_decompress_gemv_scratch_bytes(s) bytes.  Two launches on st; corrupt
+ * tiles are reported in *d_status as by df11_decompress_block.
+ */
+uint64_t df11_decompress_gemv_scratch_bytes(const df11_device_stream *s);
+int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *tensors,
+                         uint32_t n_tensors, const float *x, float *y, void *scratch,
+                         uint64_t scratch_bytes, int32_t *d_status, df11_hip_stream st);
+
 #ifdef __cplusplus
 }
 #endif
