@@ -677,7 +677,7 @@ def fused_bench(args, torch, ed, sw):
     # the rounding bound of each kernel's summation order
     yf, ys = y_f.cpu().numpy().astype(np.float64), y_s.cpu().numpy().astype(np.float64)
     bop = hs.block_out_pos.astype(np.int64)
-    per_lane = -(-(int(hs.max_tile_symbols) // 8 + 2) // 64)
+    passes = -(-(int(hs.max_tile_symbols) // 8 + 2) // 64)
     u = 2.0 ** -24
     off = xo = yo = 0
     for (rows, cols), w in zip(shapes, tensors):
@@ -688,7 +688,7 @@ def fused_bench(args, torch, ed, sw):
         starts = off + r * cols
         tiles = (np.searchsorted(bop, starts + cols - 1, side="right")
                  - np.searchsorted(bop, starts, side="right") + 1)
-        df = 8 + per_lane + 6 + tiles
+        df = 9 * passes + 2 + 7 + tiles  # the fused kernel's summation depth
         ds_ = -(-cols // 64) + 6
         ok &= bool(np.all(np.abs(yf[yo + r] - ref) <= df * u / (1 - df * u) * absum + 1e-30))
         ok &= bool(np.all(np.abs(ys[yo + r] - ref) <= ds_ * u / (1 - ds_ * u) * absum + 1e-30))

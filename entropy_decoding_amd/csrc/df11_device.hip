@@ -722,28 +722,78 @@ constexpr uint32_t kRowsPerTile = 4;
 
 struct GemvDesc {
     uint32_t n;
-    uint32_t off[DF11_GEMV_MAX_TENSORS + 1];   // first element of each matrix in the unit, then N
+    // first element of each matrix in the unit; entries n .. 16 hold N, so
+    // that the matrix of element e is the number of entries 1 .. 16 <= e
+    uint32_t off[DF11_GEMV_MAX_TENSORS + 1];
     uint32_t row0[DF11_GEMV_MAX_TENSORS + 1];  // first global row of each matrix, then the total
     uint32_t cols[DF11_GEMV_MAX_TENSORS];
+    uint32_t inv[DF11_GEMV_MAX_TENSORS];  // ceil(2^32 / cols)
     uint32_t x_off[DF11_GEMV_MAX_TENSORS], y_off[DF11_GEMV_MAX_TENSORS];
 };
 
-// matrix holding unit element g
+// matrix holding unit element e (e < N): scalar compares over the whole table
 __device__ __forceinline__ uint32_t matrix_of(const GemvDesc &g, uint32_t e) {
     uint32_t k = 0;
-    while (k + 1 < g.n && e >= g.off[k + 1]) k++;
+#pragma unroll
+    for (uint32_t m = 1; m <= DF11_GEMV_MAX_TENSORS; m++) k += uint32_t(e >= g.off[m]);
     return k;
 }
 
+// floor(v / d) for d = g.cols[k] >= 8, from inv = ceil(2^32 / d): the product's
+// high word is the quotient or one more (v < 2^32), so one correction
+__device__ __forceinline__ uint32_t div_cols(const GemvDesc &g, uint32_t k, uint32_t v) {
+    uint32_t q = __umulhi(v, g.inv[k]);
+    if (uint64_t(q) * g.cols[k] > v) q--;
+    return q;
+}
+
+// Sum over the 64 lanes of a wave, in a fixed order: rows of 16 lanes by DPP
+// (lane pairs, quads, then rotations by 4 and 8), then the four row sums of
+// lanes 0, 16, 32 and 48 in order.  The result is uniform.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x124>(v);  // row_ror:4
+    v += dpp_f<0x128>(v);  // row_ror:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return ((r0 + r1) + r2) + r3;
 }
 
 // fp32 value of a BF16 weight from its sign+mantissa byte and exponent byte
 __device__ __forceinline__ float bf16_value(uint32_t sm, uint32_t e) {
     return __uint_as_float(((sm & 0x80u) << 24) | (e << 23) | ((sm & 0x7Fu) << 16));
+}
+
+// acc + the dot product of 8 weights (sm bytes S, exponent bytes E, two words
+// each) with x[0..7], as a chain of fused multiply-adds.  Byte k of H is
+// sm.7 | e.7..1 and of L e.0 | sm.6..0, so one byte permute places the fp32
+// bits of weight k, [H_k, L_k, 0, 0].
+__device__ __forceinline__ float dot8_bf16(float acc, uint2 S, uint2 E, const float4 &x0,
+                                           const float4 &x1) {
+    const uint32_t H0 = (S.x & 0x80808080u) | ((E.x >> 1) & 0x7F7F7F7Fu);
+    const uint32_t L0 = ((E.x << 7) & 0x80808080u) | (S.x & 0x7F7F7F7Fu);
+    const uint32_t H1 = (S.y & 0x80808080u) | ((E.y >> 1) & 0x7F7F7F7Fu);
+    const uint32_t L1 = ((E.y << 7) & 0x80808080u) | (S.y & 0x7F7F7F7Fu);
+    auto w = [](uint32_t H, uint32_t L, uint32_t k) {
+        return __uint_as_float(__builtin_amdgcn_perm(H, L, ((4u + k) << 24) | (k << 16) | 0x0C0Cu));
+    };
+    acc = fmaf(w(H0, L0, 0), x0.x, acc);
+    acc = fmaf(w(H0, L0, 1), x0.y, acc);
+    acc = fmaf(w(H0, L0, 2), x0.z, acc);
+    acc = fmaf(w(H0, L0, 3), x0.w, acc);
+    acc = fmaf(w(H1, L1, 0), x1.x, acc);
+    acc = fmaf(w(H1, L1, 1), x1.y, acc);
+    acc = fmaf(w(H1, L1, 2), x1.z, acc);
+    acc = fmaf(w(H1, L1, 3), x1.w, acc);
+    return acc;
 }
 
 struct GemvEpi {
@@ -757,119 +807,118 @@ struct GemvEpi {
                                          uint32_t A0, uint32_t n8, const uint2 (&smv)[JP],
                                          const uint8_t *sm0, const uint8_t *ebuf, uint32_t lane) {
         const GemvDesc &d = *g;
+        float *pt = part + uint64_t(tile) * kRowsPerTile;
         if (P0 == P1) {  // a tile past the last code start holds no weights
-            if (lane < kRowsPerTile) part[uint64_t(tile) * kRowsPerTile + lane] = 0.0f;
+            if (lane < kRowsPerTile) pt[lane] = 0.0f;
             if (lane == 0) row_a[tile] = 0;
             return;
         }
-        // the tile's first and last rows (uniform over the wave)
+        // the tile's first row ra, and the rows it touches (uniform over the wave)
         const uint32_t ka = matrix_of(d, P0), kb = matrix_of(d, P1 - 1);
-        const uint32_t ra = d.row0[ka] + (P0 - d.off[ka]) / d.cols[ka];
-        const uint32_t rb = d.row0[kb] + (P1 - 1 - d.off[kb]) / d.cols[kb];
-        if (rb - ra >= kRowsPerTile) {
+        const uint32_t qa = div_cols(d, ka, P0 - d.off[ka]);
+        const uint32_t ra = d.row0[ka] + qa;
+        const uint32_t rb = d.row0[kb] + div_cols(d, kb, P1 - 1 - d.off[kb]);
+        const uint32_t nrows = rb - ra + 1;
+        if (nrows > kRowsPerTile) {
             // impossible for a valid unit (the host checks the widest tile
             // against the narrowest matrix); a corrupt one is reported
-            if (lane < kRowsPerTile) part[uint64_t(tile) * kRowsPerTile + lane] = 0.0f;
+            if (lane < kRowsPerTile) pt[lane] = 0.0f;
             if (lane == 0) {
                 row_a[tile] = ra;
                 if (a.status) atomicExch(a.status, int32_t(DF11_E_CORRUPT));
             }
             return;
         }
+        const uint32_t passes = (n8 + 63) / 64;  // 64-chunk passes over the tile
         float acc[kRowsPerTile] = {};
-        if (ka == kb) {
-            // rows ra .. ra+3 of one matrix start at rs, b1, b2, b3: a chunk's
-            // row and column follow from three comparisons
+        if (ka == kb && d.cols[ka] >= 512 * passes) {
+            // Rows at least as long as the span of one lane's chunks (so the
+            // tile touches at most two rows and each lane crosses at most
+            // one row start).  Lane l takes chunks l, l+64, ...: a column that
+            // advances by 512 per pass, a running sum for the lane's first row
+            // (sa) and one for the next (sb), updated by selects.
             const uint32_t cols = d.cols[ka];
-            const uint32_t rs = d.off[ka] + (ra - d.row0[ka]) * cols;
-            const uint32_t b1 = rs + cols, b2 = b1 + cols, b3 = b2 + cols;
+            const uint32_t rs = d.off[ka] + qa * cols;  // start of row ra
             const float *xk = x + d.x_off[ka];
-            // one lane's chunks lie in non-decreasing rows: a running sum per
-            // lane, moved to its row's accumulator when the row changes
-            float run = 0.0f;
-            uint32_t cur = 0;
-            auto chunk = [&](uint32_t c, uint2 s8) {
-                const uint32_t gi = A0 + 8 * c;
-                const uint32_t idx = uint32_t(gi >= b1) + uint32_t(gi >= b2) + uint32_t(gi >= b3);
-                const uint32_t r0 = gi >= b3 ? b3 : gi >= b2 ? b2 : gi >= b1 ? b1 : rs;
-                if (idx != cur) {
-#pragma unroll
-                    for (uint32_t i = 0; i < kRowsPerTile; i++) acc[i] += cur == i ? run : 0.0f;
-                    run = 0.0f;
-                    cur = idx;
-                }
-                const float4 x0 = *reinterpret_cast<const float4 *>(xk + (gi - r0));
-                const float4 x1 = *reinterpret_cast<const float4 *>(xk + (gi - r0) + 4);
-                const uint2 e8 = *reinterpret_cast<const uint2 *>(ebuf + 8 * c);
-                uint32_t wv[4];
-                assemble4(s8.x, e8.x, wv[0], wv[1]);
-                assemble4(s8.y, e8.y, wv[2], wv[3]);
-                run = fmaf(__uint_as_float(wv[0] << 16), x0.x, run);
-                run = fmaf(__uint_as_float(wv[0] & 0xFFFF0000u), x0.y, run);
-                run = fmaf(__uint_as_float(wv[1] << 16), x0.z, run);
-                run = fmaf(__uint_as_float(wv[1] & 0xFFFF0000u), x0.w, run);
-                run = fmaf(__uint_as_float(wv[2] << 16), x1.x, run);
-                run = fmaf(__uint_as_float(wv[2] & 0xFFFF0000u), x1.y, run);
-                run = fmaf(__uint_as_float(wv[3] << 16), x1.z, run);
-                run = fmaf(__uint_as_float(wv[3] & 0xFFFF0000u), x1.w, run);
+            const uint32_t cw0 = P0 == A0 ? 0u : 1u, cw1 = (P1 - A0) / 8;  // whole chunks
+            uint32_t col0 = A0 + 8 * lane - rs;
+            const bool first_next = col0 >= cols;  // the lane's first chunk is in row ra+1
+            col0 -= first_next ? cols : 0u;
+            // pass j: column col0 + 512 j, one row further once that reaches
+            // cols (below 2 cols, since 512 passes <= cols: one wrap at most)
+            float sa = 0.0f, sb = 0.0f;
+            auto pass = [&](uint32_t j, uint2 s8) {
+                const uint32_t c = lane + 64 * j;
+                const uint32_t v = col0 + 512 * j;
+                const bool wrapped = v >= cols;
+                const float *xp = xk + (wrapped ? v - cols : v);
+                const float4 x0 = *reinterpret_cast<const float4 *>(xp);
+                const float4 x1 = *reinterpret_cast<const float4 *>(xp + 4);
+                const bool ok = c >= cw0 && c < cw1;
+                const uint2 e8 = *reinterpret_cast<const uint2 *>(ebuf + 8 * min(c, n8 - 1));
+                const float t = dot8_bf16(wrapped ? sb : sa, s8, e8, x0, x1);
+                sa = ok && !wrapped ? t : sa;
+                sb = ok && wrapped ? t : sb;
             };
-            // whole chunks
 #pragma unroll
-            for (int j = 0; j < JP; j++) {
-                const uint32_t c = lane + j * 64;
-                const uint32_t gi = A0 + 8 * c;
-                if (c < n8 && gi >= P0 && gi + 8 <= P1) chunk(c, smv[j]);
+            for (int j = 0; j < JP; j++) pass(j, smv[j]);
+            for (uint32_t j = JP; j < passes; j++) {
+                const uint32_t c = min(lane + 64 * j, n8 - 1);
+                pass(j, *reinterpret_cast<const uint2 *>(sm0 + 8 * c));
             }
-            for (uint32_t c = lane + JP * 64; c < n8; c += 64) {
-                const uint32_t gi = A0 + 8 * c;
-                if (gi >= P0 && gi + 8 <= P1) chunk(c, *reinterpret_cast<const uint2 *>(sm0 + 8 * c));
-            }
-#pragma unroll
-            for (uint32_t i = 0; i < kRowsPerTile; i++) acc[i] += cur == i ? run : 0.0f;
+            // rows relative to ra: sa is row first_next, sb the row after
+            acc[0] = first_next ? 0.0f : sa;
+            acc[1] = first_next ? sa : sb;
             // the chunks holding P0 and P1-1 when they are not whole, one
             // element per lane (lanes 0-7 and 8-15; once if they coincide)
-            const uint32_t ch = (P0 - A0) / 8, ct = (P1 - 1 - A0) / 8;
-            const uint2 sh = chunk_sm<JP, FMT>(a, smv, A0, ch), sl = chunk_sm<JP, FMT>(a, smv, A0, ct);
-            if (lane < 16 && (lane < 8 || ct != ch)) {
-                const uint32_t c = lane < 8 ? ch : ct, k = lane & 7u;
-                const uint32_t gi = A0 + 8 * c, i = gi + k;
-                const bool whole = gi >= P0 && gi + 8 <= P1;
-                if (!whole && i >= P0 && i < P1) {
-                    const uint2 s8 = lane < 8 ? sh : sl;
-                    const uint32_t sb = ((k < 4 ? s8.x : s8.y) >> (8 * (k & 3u))) & 0xFFu;
-                    const float w = bf16_value(sb, ebuf[8 * c + k]);
-                    const uint32_t idx = uint32_t(i >= b1) + uint32_t(i >= b2) + uint32_t(i >= b3);
-                    const uint32_t r0 = i >= b3 ? b3 : i >= b2 ? b2 : i >= b1 ? b1 : rs;
-                    const float xv = xk[i - r0];
-#pragma unroll
-                    for (uint32_t q = 0; q < kRowsPerTile; q++)
-                        if (idx == q) acc[q] = fmaf(w, xv, acc[q]);
+            const uint32_t ch = 0, ct = n8 - 1;
+            const bool edge_h = cw0 > 0 || cw1 == 0, edge_t = ct >= cw1 && ct != ch;
+            if (edge_h || edge_t) {
+                const uint2 sh = chunk_sm<JP, FMT>(a, smv, A0, ch), sl = chunk_sm<JP, FMT>(a, smv, A0, ct);
+                if (lane < 16) {
+                    const uint32_t c = lane < 8 ? ch : ct, k = lane & 7u;
+                    const uint32_t i = A0 + 8 * c + k;
+                    if ((lane < 8 ? edge_h : edge_t) && i >= P0 && i < P1) {
+                        const uint2 s8 = lane < 8 ? sh : sl;
+                        const uint32_t sb8 = ((k < 4 ? s8.x : s8.y) >> (8 * (k & 3u))) & 0xFFu;
+                        const float w = bf16_value(sb8, ebuf[8 * c + k]);
+                        const bool next = i - rs >= cols;
+                        const float xv = xk[i - rs - (next ? cols : 0u)];
+                        if (next) acc[1] = fmaf(w, xv, acc[1]);
+                        else acc[0] = fmaf(w, xv, acc[0]);
+                    }
                 }
             }
         } else {
-            // a tile that spans matrices (at most one per matrix boundary):
+            // short rows (up to four per tile) or a tile that spans matrices:
             // element by element
             for (uint32_t i = P0 + lane; i < P1; i += 64) {
                 const uint32_t k = matrix_of(d, i);
                 const uint32_t rel = i - d.off[k];
-                const uint32_t idx = d.row0[k] + rel / d.cols[k] - ra;
+                const uint32_t q = div_cols(d, k, rel);
+                const uint32_t idx = d.row0[k] + q - ra;
                 const float w = bf16_value(a.sm[i], ebuf[i - A0]);
-                const float xv = x[d.x_off[k] + rel % d.cols[k]];
+                const float xv = x[d.x_off[k] + rel - q * d.cols[k]];
 #pragma unroll
-                for (uint32_t q = 0; q < kRowsPerTile; q++)
-                    if (idx == q) acc[q] = fmaf(w, xv, acc[q]);
+                for (uint32_t r = 0; r < kRowsPerTile; r++)
+                    if (idx == r) acc[r] = fmaf(w, xv, acc[r]);
             }
         }
+        // the row sums of the rows the tile touches; lanes 0..3 store them
+        float mine = 0.0f;
 #pragma unroll
         for (uint32_t i = 0; i < kRowsPerTile; i++) {
-            const float s = wave_sum_f(acc[i]);
-            if (lane == 0) part[uint64_t(tile) * kRowsPerTile + i] = s;
+            if (i < nrows) {
+                const float s = wave_sum_f(acc[i]);
+                if (lane == i) mine = s;
+            }
         }
+        if (lane < kRowsPerTile) pt[lane] = mine;
         if (lane == 0) row_a[tile] = ra;
     }
 };
 
-__global__ __launch_bounds__(kThreads) void df11_decode_gemv(KArgs a, GemvDesc d, const float *x,
+__global__ __launch_bounds__(kThreads, 7) void df11_decode_gemv(KArgs a, GemvDesc d, const float *x,
                                                              float *part, uint32_t *row_a) {
     GemvEpi epi{&d, x, part, row_a};
     wave_tiles<4, DF11_FORMAT_BF16>(a, epi);
@@ -1056,6 +1105,7 @@ int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t,
         d.off[k] = uint32_t(off);
         d.row0[k] = uint32_t(row);
         d.cols[k] = t[k].cols;
+        d.inv[k] = uint32_t(((uint64_t(1) << 32) + t[k].cols - 1) / t[k].cols);
         d.x_off[k] = uint32_t(t[k].x_offset);
         d.y_off[k] = uint32_t(t[k].y_offset);
         if (t[k].x_offset >= (uint64_t(1) << 32) || t[k].y_offset >= (uint64_t(1) << 32))
@@ -1065,7 +1115,7 @@ int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t,
         min_cols = std::min(min_cols, t[k].cols);
     }
     if (off != s->n_weights || row >= (uint64_t(1) << 32)) return DF11_E_INVALID;
-    d.off[n_tensors] = uint32_t(off);
+    for (uint32_t k = n_tensors; k <= DF11_GEMV_MAX_TENSORS; k++) d.off[k] = uint32_t(off);
     d.row0[n_tensors] = uint32_t(row);
     // a tile of M outputs touches at most (M - 1) / min_cols + 2 rows
     if (s->max_tile_symbols > 0 && (s->max_tile_symbols - 1) / min_cols + 2 > kRowsPerTile)

@@ -33,20 +33,23 @@ def _bf16(rng, n, sigma=0.02):
 
 
 def _depth_per_row(hs, shapes):
-    """Roundings on the longest path into each output.  In a tile, one lane
-    chains fused multiply-adds over its whole 8-weight chunks of a row (at
-    most ceil(chunks per tile / 64) chunks), adds that to the row's sum, and
-    may add one edge weight; then 6 butterfly levels, and one addition per
-    tile holding the row.  A tile spanning two matrices chains at most
-    ceil(weights per tile / 64) products per lane, which is fewer."""
+    """Roundings on the longest path into each output.  In a tile a lane's
+    64-chunk passes number at most P = ceil(chunks per tile / 64); it chains
+    fused multiply-adds over its whole 8-weight chunks of a row (at most 8P),
+    and the row's accumulator receives at most P + 2 additions (the running
+    sum, chunk sums of passes that cross a row start, one edge weight).  A
+    tile spanning two matrices chains at most ceil(weights / 64) <= 8P
+    products per lane.  Then 7 levels of the wave sum (4 within rows of 16
+    lanes, 3 over the row sums) and one addition per tile holding the row."""
     bop = hs.block_out_pos.astype(np.int64)
-    per_lane = 8 * -(-(int(hs.max_tile_symbols) // 8 + 2) // 64) + 2
+    passes = -(-(int(hs.max_tile_symbols) // 8 + 2) // 64)
+    per_lane = 9 * passes + 2
     out, off = [], 0
     for rows, cols in shapes:
         starts = off + np.arange(rows, dtype=np.int64) * cols
         t0 = np.searchsorted(bop, starts, side="right") - 1
         t1 = np.searchsorted(bop, starts + cols - 1, side="right") - 1
-        out.append(per_lane + 6 + (t1 - t0 + 1))
+        out.append(per_lane + 7 + (t1 - t0 + 1))
         off += rows * cols
     return np.concatenate(out)
 
