@@ -924,6 +924,33 @@ __global__ __launch_bounds__(kThreads, 7) void df11_decode_gemv(KArgs a, GemvDes
     wave_tiles<4, DF11_FORMAT_BF16>(a, epi);
 }
 
+// The tile holding unit element e: the largest t with bop[t] <= e, given
+// bop[lo] <= e < bop[hi].  Output positions grow almost linearly with the
+// tile index within a matrix, so each step probes where e falls by linear
+// interpolation, and every other step halves the range (at most twice the
+// steps of a plain bisection on any input).
+__device__ __forceinline__ uint32_t tile_of(const uint32_t *bop, uint32_t e, uint32_t lo,
+                                            uint32_t hi) {
+    uint32_t blo = bop[lo], bhi = bop[hi];
+    for (uint32_t step = 0; hi - lo > 1; step++) {
+        uint32_t mid = lo + (hi - lo) / 2;
+        if ((step & 1) == 0 && bhi > blo) {
+            const uint64_t f = uint64_t(e - blo) * (hi - lo) / (bhi - blo);
+            mid = lo + uint32_t(f);
+            mid = mid <= lo ? lo + 1 : mid >= hi ? hi - 1 : mid;
+        }
+        const uint32_t bm = bop[mid];
+        if (bm <= e) {
+            lo = mid;
+            blo = bm;
+        } else {
+            hi = mid;
+            bhi = bm;
+        }
+    }
+    return lo;
+}
+
 // y for every row: the sums of the tiles that hold it, in tile order.
 __global__ __launch_bounds__(kThreads) void df11_gemv_rows(GemvDesc d, const uint32_t *bop,
                                                            uint32_t n_tiles, const float *part,
@@ -933,25 +960,27 @@ __global__ __launch_bounds__(kThreads) void df11_gemv_rows(GemvDesc d, const uin
     uint32_t k = 0;
     while (k + 1 < d.n && r >= d.row0[k + 1]) k++;
     const uint32_t rs = d.off[k] + (r - d.row0[k]) * d.cols[k], re = rs + d.cols[k] - 1;
-    // the tiles holding elements rs and re: largest t with bop[t] <= element
-    auto tile_of = [&](uint32_t e) {
-        uint32_t lo = 0, hi = n_tiles;  // bop[lo] <= e < bop[hi]
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) / 2;
-            if (bop[mid] <= e) lo = mid;
-            else hi = mid;
-        }
-        return lo;
-    };
-    const uint32_t t0 = tile_of(rs), t1 = tile_of(re);
-    float s = 0.0f;
-    // row_a of a tile skipped as corrupt was never written: the index is
-    // checked so that such a unit yields wrong sums (and its status), never
-    // a read outside part
-    for (uint32_t t = t0; t <= t1; t++) {
-        const uint32_t i = r - row_a[t];
-        if (i < kRowsPerTile) s += part[uint64_t(t) * kRowsPerTile + i];
+    // bop[0] = 0 <= rs and re < N = bop[n_tiles] for a valid unit; a corrupt
+    // bop only yields other (wrong) tiles in [0, n_tiles)
+    const uint32_t t0 = bop[n_tiles] > rs ? tile_of(bop, rs, 0, n_tiles) : n_tiles - 1;
+    // the last tile of the row is a few tiles further: widen by doubling
+    uint32_t lo = t0, span = 1;
+    while (lo + span < n_tiles && bop[lo + span] <= re) {
+        lo += span;
+        span *= 2;
     }
+    const uint32_t t1 = lo + span < n_tiles ? tile_of(bop, re, lo, lo + span)
+                                            : (bop[n_tiles] > re ? tile_of(bop, re, lo, n_tiles)
+                                                                 : n_tiles - 1);
+    // Tiles after t0 start inside the row (rs < bop[t] <= re), so the row is
+    // their first: slot 0, and their loads do not wait for one another.
+    // row_a of a tile skipped as corrupt was never written: t0's slot is
+    // checked so that such a unit yields wrong sums (and its status), never
+    // a read outside part.
+    const uint32_t i0 = r - row_a[t0];
+    float s = i0 < kRowsPerTile ? part[uint64_t(t0) * kRowsPerTile + i0] : 0.0f;
+#pragma unroll 4
+    for (uint32_t t = t0 + 1; t <= t1; t++) s += part[uint64_t(t) * kRowsPerTile];
     y[d.y_off[k] + (r - d.row0[k])] = s;
 }
 

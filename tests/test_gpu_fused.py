@@ -163,3 +163,35 @@ def test_fused_gemv_corrupt_unit_is_reported():
     ed.df11_decompress_gemv(ds, layout, x, y, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == ed.DF11_E_CORRUPT
+
+
+def test_fused_gemv_scratch_needs_no_initialisation():
+    """The workspace's previous contents (any bytes, or another unit's
+    indices) do not change the results."""
+    rng = np.random.default_rng(14)
+    shapes = [(40, 4096), (24, 2048)]
+    tensors = [_bf16(rng, r * c) for r, c in shapes]
+    cb = ed.df11_build_codebook(tensors)
+    ds = ed.DeviceStream(ed.df11_encode(cb, tensors, 64, 8), cb, "cuda")
+    layout = ed.gemv_layout(shapes)
+    x = torch.from_numpy(rng.standard_normal(layout[2]).astype(np.float32)).cuda()
+    need = int(ed.LIB.df11_decompress_gemv_scratch_bytes(ed.ctypes.byref(ds.desc)))
+    ys = []
+    for fill in ("zeros", "ones", "random"):
+        if fill == "zeros":
+            scr = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        elif fill == "ones":
+            scr = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+        else:
+            scr = torch.from_numpy(rng.integers(0, 256, need, dtype=np.uint8)).cuda()
+        y = torch.full((layout[3],), float("nan"), device="cuda")
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        say(f"[gpu] df11_decompress_gemv scratch={fill}")
+        ed.df11_decompress_gemv(ds, layout, x, y, scr, st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        ys.append(y)
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+    with pytest.raises(ed.Df11Error):  # one byte short
+        ed.df11_decompress_gemv(ds, layout, x, ys[0], torch.zeros(need - 1, dtype=torch.uint8,
+                                                                  device="cuda"))
