@@ -12,6 +12,7 @@ and the CPU oracle's bit-serial decode timed on this host as a baseline.
   python bench.py [--steps K] [--warmup W] [--config 2|1|0|3a|3b|3c|4] [--tile-windows 64|256|512]
   python bench.py --pipeline     # 8B model blocks, next block decompressed while a GEMV reads this one
   python bench.py --fused        # y = W x straight from the compressed block vs decompress + GEMV
+  python bench.py --fused-gemm   # Y = X W^T for 16-64 tokens on the matrix cores, same comparison
 """
 
 from __future__ import annotations
@@ -198,6 +199,11 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="time the fused decode + GEMV on the workload's block against "
                          "decompression followed by a GEMV, and a GEMV on resident BF16")
+    ap.add_argument("--fused-gemm", action="store_true",
+                    help="time the fused decode + GEMM (matrix cores) on the workload's block "
+                         "against decompression followed by a library GEMM")
+    ap.add_argument("--tokens", type=int, default=64, choices=(16, 32, 48, 64),
+                    help="tokens for --fused-gemm")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decoder needs no cross-GPU exchange (each GPU "
@@ -219,6 +225,8 @@ def main():
         return encode_bench(args, torch, ed, sw)
     if args.fused:
         return fused_bench(args, torch, ed, sw)
+    if args.fused_gemm:
+        return fused_gemm_bench(args, torch, ed, sw)
     if args.format != "bf16" and (args.tile_windows != 64 or args.config in ("4",)):
         print("FP8 workloads use 64-window tiles and single-unit configs", file=sys.stderr)
         sys.exit(2)
@@ -711,6 +719,130 @@ def fused_bench(args, torch, ed, sw):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": read_bytes + vec_bytes},
+    }
+    print(json.dumps(line), flush=True)
+    if not ok:
+        sys.exit(1)
+
+
+def fused_gemm_bench(args, torch, ed, sw):
+    """One block's products Y_k = X_k W_k^T for n tokens (BF16 X, float32 Y)
+    three ways: the fused kernel on the matrix cores reading only the
+    compressed block (encoded in GEMM order), decompression to BF16 followed by
+    a library GEMM per matrix (torch.mm, BF16 out), and that GEMM on resident
+    BF16 weights.  HIP events on the launch stream; caches evicted between
+    steps when the block fits in them."""
+    import oracle
+
+    dev = torch.device("cuda:0")
+    n = args.tokens
+    cfg = sw.config(args.config)
+    unit = cfg.units[0]
+    shapes = [shape for _, shape in unit.tensors]
+    tensors = sw.gen_unit(unit)
+    t0 = time.perf_counter()
+    ordered = [ed.df11_gemm_order(t, r, c) for t, (r, c) in zip(tensors, shapes)]
+    cbg = ed.df11_build_codebook(ordered)
+    hsg = ed.df11_encode(cbg, ordered, 64, 8)
+    dsg = ed.DeviceStream(hsg, cbg, dev)
+    del ordered
+    cb = ed.df11_build_codebook(tensors)
+    hs = ed.df11_encode(cb, tensors, 64, 8)
+    ds = ed.DeviceStream(hs, cb, dev)
+    log(f"[bench] fused gemm: {cfg.name} encoded twice (GEMM and row order) in "
+        f"{time.perf_counter() - t0:.1f} s, {hsg.n_tiles} tiles")
+    nw = hs.n_weights
+    layout = ed.gemm_layout(shapes, n)
+    rng = np.random.default_rng(6)
+    xh = ((rng.standard_normal(layout[2]).astype(np.float32).view(np.uint32) >> 16)
+          .astype(np.uint16))
+    x = torch.from_numpy(xh.view(np.int16)).to(dev)
+    y_f = torch.zeros(layout[3], dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    buf = torch.empty(nw, dtype=torch.bfloat16, device=dev)
+    w_res = torch.from_numpy(np.concatenate(tensors).view(np.int16)).to(dev).view(torch.bfloat16)
+    offs = np.cumsum([0] + [r * c for r, c in shapes])
+    xoffs = np.cumsum([0] + [n * c for _, c in shapes])
+    xb = x.view(torch.bfloat16)
+    xs = [xb[xoffs[k]:xoffs[k + 1]].view(n, c) for k, (_, c) in enumerate(shapes)]
+    outs = [torch.empty((n, r), dtype=torch.bfloat16, device=dev) for r, _ in shapes]
+    stream = torch.cuda.current_stream()
+    # compressed unit read once, activations read once, products written once
+    alg = algorithmic_bytes(hsg, cbg) - 2 * nw + 2 * layout[2] + 4 * layout[3]
+    small = algorithmic_bytes(hs, cb) < (1 << 30)
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if small else None
+    sink = torch.zeros((), dtype=torch.int32, device=dev)
+
+    scratch = torch.empty(ed.df11_decompress_gemm_scratch_bytes(layout, n), dtype=torch.uint8,
+                          device=dev)
+
+    def fused():
+        ed.df11_decompress_gemm(dsg, layout, n, x, y_f, scratch, status, stream)
+
+    def mm(wbuf):
+        for k, (r, c) in enumerate(shapes):
+            torch.mm(xs[k], wbuf[offs[k]:offs[k + 1]].view(r, c).t(), out=outs[k])
+
+    def sequential():
+        ed.df11_decompress_block(ds, buf, status, stream)
+        mm(buf)
+
+    def resident():
+        mm(w_res)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            if flush is not None:
+                torch.amax(flush, dim=0, out=sink)
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    res = {name: timed(fn) for name, fn in
+           (("fused", fused), ("decompress_then_gemm", sequential), ("bf16_gemm", resident))}
+    ok = int(status.item()) == 0 and torch.equal(buf.view(torch.int16), w_res.view(torch.int16))
+    # sampled rows of every matrix against the oracle's float64 product, within
+    # a bound that assumes nothing about the matrix cores' order of additions
+    yf = y_f.cpu().numpy().astype(np.float64)
+    u = 2.0 ** -24
+    yo = 0
+    for k, ((r, c), w) in enumerate(zip(shapes, tensors)):
+        rows = np.unique(np.linspace(0, r - 1, 32).astype(np.int64))
+        W = w.reshape(r, c)[rows]
+        X = xh[xoffs[k]:xoffs[k + 1]]
+        ref = oracle.gemm(W.reshape(-1), [(rows.size, c)], X, n).reshape(n, rows.size)
+        d = c + c // 32 + 3
+        bound = 2 * d * u / (1 - 2 * d * u) * (
+            np.abs(oracle.bf16_to_f64(X)).reshape(n, c) @ np.abs(oracle.bf16_to_f64(W.reshape(-1)))
+            .reshape(rows.size, c).T)
+        got = yf[yo:yo + n * r].reshape(n, r)[:, rows]
+        ok &= bool(np.all(np.abs(got - ref) <= bound + 1e-30))
+        yo += n * r
+    f = res["fused"]
+    achieved = alg / (f.mean() * 1e-3) / 1e9
+    flops = 2.0 * nw * n
+    line = {
+        "metric": "fused decompress+GEMM time per block",
+        "value": round(float(f.mean()), 4), "unit": "ms per block", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+        "vs_baseline": None, "dtype": "bf16 x bf16 -> f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "n_weights": nw, "tokens": n, "layout": "T64xB8, GEMM order",
+                   "within_rounding_bound": bool(ok), "caches_flushed_between_steps": small},
+        "ms": {k: {"mean": round(float(v.mean()), 4), "p50": round(float(np.percentile(v, 50)), 4)}
+               for k, v in res.items()},
+        "speedup_vs_decompress_then_gemm": round(float(res["decompress_then_gemm"].mean() / f.mean()), 3),
+        "speedup_vs_bf16_gemm": round(float(res["bf16_gemm"].mean() / f.mean()), 3),
+        "matrix_core_tflops": round(flops / (f.mean() * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": int(alg)},
     }
     print(json.dumps(line), flush=True)
     if not ok:

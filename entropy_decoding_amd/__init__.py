@@ -144,7 +144,7 @@ DF11_GEMV_MAX_TENSORS = 16
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run entropy_decoding_amd.build.build_library()")
+        raise ImportError(f"{LIB_PATH} is not built; run python entropy_decoding_amd/build.py")
     # PyTorch ships its own libamdhip64 (soname libamdhip64.so.7).  Loading torch
     # first lets the dynamic loader satisfy libdf11's dependency with that same
     # runtime; loading libdf11 first would bring in a second HIP runtime, whose
@@ -186,6 +186,13 @@ def _load():
     L.df11_decompress_gemv.argtypes = [ctypes.POINTER(df11_device_stream),
                                        ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32, vp, vp,
                                        vp, ctypes.c_uint64, vp, vp]
+    L.df11_gemm_order.argtypes = [_u16p, ctypes.c_uint32, ctypes.c_uint32, _u16p]
+    L.df11_decompress_gemm_scratch_bytes.argtypes = [ctypes.POINTER(df11_gemv_tensor),
+                                                     ctypes.c_uint32, ctypes.c_uint32]
+    L.df11_decompress_gemm_scratch_bytes.restype = ctypes.c_uint64
+    L.df11_decompress_gemm.argtypes = [ctypes.POINTER(df11_device_stream),
+                                       ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32,
+                                       ctypes.c_uint32, vp, vp, vp, ctypes.c_uint64, vp, vp]
     L.df11_encode_size_from_counts.argtypes = [ctypes.c_uint32, ctypes.POINTER(df11_codebook),
                                                _u64p, ctypes.c_uint64, ctypes.c_uint32,
                                                ctypes.c_uint32, ctypes.POINTER(df11_sizes)]
@@ -202,7 +209,7 @@ def _load():
               L.df11_pipeline_destroy, L.df11_pipeline_decompress, L.df11_pipeline_acquire,
               L.df11_pipeline_release, L.df11_gemv_bf16, L.df11_build_codebook_from_counts,
               L.df11_encode_size_from_counts, L.df11_histogram_device, L.df11_encode_device,
-              L.df11_decompress_gemv):
+              L.df11_decompress_gemv, L.df11_gemm_order, L.df11_decompress_gemm):
         f.restype = ctypes.c_int
     return L
 
@@ -506,6 +513,63 @@ def df11_gemv_bf16(w, layout, x, y, stream=None) -> None:
     _check("df11_gemv_bf16",
            LIB.df11_gemv_bf16(ctypes.c_void_p(w.data_ptr()), arr, n, ctypes.c_void_p(x.data_ptr()),
                               ctypes.c_void_p(y.data_ptr()), _stream_handle(stream)))
+
+
+def df11_gemm_order(w, rows: int, cols: int) -> np.ndarray:
+    """The host permutation df11_decompress_gemm expects (see include/df11.h):
+    16-row blocks of 32-column sub-blocks, each in the matrix cores' lane
+    order (four 8-column quarters of 16 rows of 8 weights)."""
+    src = np.ascontiguousarray(np.asarray(w).reshape(-1)).view(np.uint16)
+    if src.size != rows * cols:
+        raise ValueError("w must hold rows * cols weights")
+    out = np.empty(rows * cols, dtype=np.uint16)
+    _check("df11_gemm_order", LIB.df11_gemm_order(src.ctypes.data_as(_u16p), rows, cols,
+                                                  out.ctypes.data_as(_u16p)))
+    return out
+
+
+def gemm_layout(shapes, n_tokens: int):
+    """df11_gemv_tensor descriptors for df11_decompress_gemm: matrices back to
+    back in the unit, and for each a token-major x slice (n_tokens x cols,
+    BF16) and y slice (n_tokens x rows, float32), also back to back."""
+    descs, w, x, y = [], 0, 0, 0
+    for rows, cols in shapes:
+        descs.append((w, x, y, rows, cols))
+        w += rows * cols
+        x += n_tokens * cols
+        y += n_tokens * rows
+    arr = (df11_gemv_tensor * max(len(descs), 1))()
+    for i, (wo, xo, yo, r, c) in enumerate(descs):
+        arr[i].w_offset, arr[i].x_offset, arr[i].y_offset, arr[i].rows, arr[i].cols = wo, xo, yo, r, c
+    return arr, len(descs), x, y
+
+
+def df11_decompress_gemm_scratch_bytes(layout, n_tokens: int) -> int:
+    arr, n, _, _ = layout
+    return int(LIB.df11_decompress_gemm_scratch_bytes(arr, n, n_tokens))
+
+
+def df11_decompress_gemm(ds: DeviceStream, layout, n_tokens: int, x, y, scratch=None,
+                         status=None, stream=None) -> None:
+    """y = W x for n_tokens tokens per matrix of ``layout`` (from gemm_layout)
+    on the matrix cores, straight from the compressed unit ``ds`` (encoded
+    from df11_gemm_order weights).  x: 16-bit device tensor (BF16 bits), y:
+    float32 device tensor; ``scratch``: a device uint8 tensor of
+    df11_decompress_gemm_scratch_bytes bytes, allocated here when not given."""
+    import torch
+
+    arr, n, nx, ny = layout
+    if x.element_size() != 2 or y.dtype.itemsize != 4 or x.numel() < nx or y.numel() < ny:
+        raise ValueError("x must be a 16-bit and y a float32 device tensor covering the layout")
+    need = df11_decompress_gemm_scratch_bytes(layout, n_tokens)
+    if scratch is None:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
+    _check("df11_decompress_gemm",
+           LIB.df11_decompress_gemm(ctypes.byref(ds.desc), arr, n, n_tokens,
+                                    ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                    ctypes.c_void_p(scratch.data_ptr()), scratch.numel(), sp,
+                                    _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------- device encoder

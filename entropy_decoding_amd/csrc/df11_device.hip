@@ -580,19 +580,23 @@ __device__ __forceinline__ uint2 chunk_sm(const KArgs &a, const uint2 (&smv)[JP]
 // weight format (BF16 or FP8): only the final assembly differs.
 //
 // Epi is what happens to a decoded tile: StoreEpi writes the weights, the
-// fused GEMV consumes them (df11_decompress_gemv).
+// fused GEMV and GEMM consume them (df11_decompress_gemv, _gemm).  Epi::kSmv
+// says whether the tile's sign+mantissa bytes are loaded in lane order
+// (chunk lane + 64 j in smv[j]) before the decode; Epi::prefetch may load
+// whatever else the epilogue needs at that point.  The wave takes tiles
+// first + slot, first + slot + n_slots, ... below first + count.
 template <int JP, int FMT, class Epi>
-__device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi) {
+__device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi, uint32_t first,
+                                           uint32_t count, uint32_t slot, uint32_t n_slots) {
     using F = OutFmt<FMT>;
     constexpr uint32_t CH = F::kChunk;
     __shared__ __align__(16) uint8_t fast[kLutOff];
     extern __shared__ __align__(16) uint8_t dyn[];
     constexpr uint32_t W = 64;  // windows per tile
     const uint32_t t = threadIdx.x, lane = t & 63u, wid = t >> 6;
-    const uint32_t slot = 4 * xcd_grouped(blockIdx.x) + wid, n_slots = 4 * gridDim.x;
 
     TileIn<1> cur;
-    if (slot < a.n_tiles) cur.load<W>(a, a.tile0 + slot, lane);
+    if (slot < count) cur.load<W>(a, first + slot, lane);
     for (uint32_t i = 16 * t; i < a.lds_tables; i += 16 * kThreads) {
         const uint4 v = *reinterpret_cast<const uint4 *>(a.tables + (i < kLutOff ? i : i + 512));
         *reinterpret_cast<uint4 *>(i < kLutOff ? fast + i : dyn + (i - kLutOff)) = v;
@@ -601,8 +605,8 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi) {
     const uint16_t *lut = reinterpret_cast<const uint16_t *>(dyn);
     uint8_t *ebuf = dyn + a.ebuf_off + wid * a.exp_cap;
 
-    for (uint32_t it = slot; it < a.n_tiles; it += n_slots) {
-        const uint32_t tile = a.tile0 + it;
+    for (uint32_t it = slot; it < count; it += n_slots) {
+        const uint32_t tile = first + it;
         const uint32_t P0 = __builtin_amdgcn_readlane(cur.bounds, 0);
         const uint32_t P1 = __builtin_amdgcn_readlane(cur.bounds, 1);
         const uint32_t A0 = P0 & ~(CH - 1);
@@ -610,13 +614,16 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi) {
         const uint32_t n8 = sane ? (P1 - A0 + CH - 1) / CH : 0;  // chunks
         const uint8_t *sm0 = a.sm + F::rest_off(A0);
         uint2 smv[JP];
+        if constexpr (Epi::kSmv) {
 #pragma unroll
-        for (int j = 0; j < JP; j++) {
-            const uint32_t c = lane + j * 64;
-            if (c < n8) smv[j] = *reinterpret_cast<const uint2 *>(sm0 + 8 * c);
+            for (int j = 0; j < JP; j++) {
+                const uint32_t c = lane + j * 64;
+                if (c < n8) smv[j] = *reinterpret_cast<const uint2 *>(sm0 + 8 * c);
+            }
         }
+        if (sane) epi.prefetch(a, P0, P1, lane);
         TileIn<1> nxt;
-        nxt.load<W>(a, a.tile0 + min(it + n_slots, a.n_tiles - 1), lane);
+        nxt.load<W>(a, first + min(it + n_slots, count - 1), lane);
 
         uint32_t d[3];
 #pragma unroll
@@ -667,6 +674,8 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi) {
 }
 
 struct StoreEpi {
+    static constexpr bool kSmv = true;
+    __device__ __forceinline__ void prefetch(const KArgs &, uint32_t, uint32_t, uint32_t) {}
     template <int JP, int FMT>
     __device__ __forceinline__ void tile(const KArgs &a, uint32_t, uint32_t P0, uint32_t P1,
                                          uint32_t A0, uint32_t n8, const uint2 (&smv)[JP],
@@ -700,6 +709,15 @@ struct StoreEpi {
         }
     }
 };
+
+// the grid's waves over the tiles tile0 .. tile0 + n_tiles - 1, in the
+// XCD-grouped order
+template <int JP, int FMT, class Epi>
+__device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi) {
+    const uint32_t wid = threadIdx.x >> 6;
+    wave_tiles<JP, FMT>(a, epi, a.tile0, a.n_tiles, 4 * xcd_grouped(blockIdx.x) + wid,
+                        4 * gridDim.x);
+}
 
 template <int JP, int FMT>
 __global__ __launch_bounds__(kThreads) void df11_decode_wave(KArgs a) {
@@ -797,6 +815,8 @@ __device__ __forceinline__ float dot8_bf16(float acc, uint2 S, uint2 E, const fl
 }
 
 struct GemvEpi {
+    static constexpr bool kSmv = true;
+    __device__ __forceinline__ void prefetch(const KArgs &, uint32_t, uint32_t, uint32_t) {}
     const GemvDesc *g;
     const float *x;
     float *part;     // kRowsPerTile row sums per tile
@@ -982,6 +1002,195 @@ __global__ __launch_bounds__(kThreads) void df11_gemv_rows(GemvDesc d, const uin
 #pragma unroll 4
     for (uint32_t t = t0 + 1; t <= t1; t++) s += part[uint64_t(t) * kRowsPerTile];
     y[d.y_off[k] + (r - d.row0[k])] = s;
+}
+
+// ---------------------------------------------------------------- fused GEMM
+//
+// Y^T = X^T W^T for the matrices of a BF16 unit and n = 16 NB tokens, straight
+// from the compressed stream, on the matrix cores.  The unit holds each
+// matrix in GEMM order (df11_gemm_order): 16-row blocks, each as 32-column
+// sub-blocks of 16 x 32 weights in the lane order of the A operand of
+// v_mfma_f32_16x16x32_bf16 (lane l: row l % 16, columns 8 (l / 16) .. +7), so
+// lane l takes the sub-block's 8-weight chunk l and a wave reads a
+// sub-block's sign+mantissa bytes and staged exponents contiguously.  The
+// activations are first reordered the same way for the B operand (lane l:
+// token l % 16 of a 16-token group, columns 8 (l / 16) .. +7 of the
+// sub-block): per matrix, [32-column block][quarter][token][8], so 16
+// neighbouring lanes read 256 contiguous bytes.  One workgroup owns one
+// 16-row block: its four waves
+// decode the tiles holding the block (the first and last are shared with
+// the neighbouring blocks, and decoded by both), each wave accumulating its
+// sub-blocks' products; weights of a chunk outside the tile are zeroed.  The
+// four waves' sums are added in a fixed order at the end.
+
+constexpr uint32_t kGemmPre = 4;  // sub-blocks whose sm bytes are loaded before the decode
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+struct GemmDesc {
+    uint32_t n;
+    uint32_t mb0[DF11_GEMV_MAX_TENSORS + 1];  // first row block of each matrix; n .. 16: the total
+    uint32_t off[DF11_GEMV_MAX_TENSORS];      // first element of each matrix in the unit
+    uint32_t rows[DF11_GEMV_MAX_TENSORS], cols[DF11_GEMV_MAX_TENSORS];
+    uint32_t x_off[DF11_GEMV_MAX_TENSORS], y_off[DF11_GEMV_MAX_TENSORS];
+    // reordered activations: 16-byte chunks ch0[k] .. ch0[k+1]-1 of the workspace
+    uint32_t ch0[DF11_GEMV_MAX_TENSORS + 1];  // n .. 16: the total
+};
+
+// The activations in the B operand's order: chunk j of matrix k's slice is
+// tokens' columns [32 kb + 8 q, +8) with t = j % T, q = (j / T) % 4,
+// kb = j / (4 T), T = 16 NB tokens.  One thread per 16-byte chunk.
+__global__ __launch_bounds__(kThreads) void df11_gemm_x_order(GemmDesc g, uint32_t n_tok,
+                                                              const uint16_t *x, uint16_t *xs) {
+    const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
+    if (j >= g.ch0[DF11_GEMV_MAX_TENSORS]) return;
+    uint32_t k = 0;
+#pragma unroll
+    for (uint32_t m = 1; m <= DF11_GEMV_MAX_TENSORS; m++) k += uint32_t(j >= g.ch0[m]);
+    const uint32_t r = j - g.ch0[k];
+    const uint32_t t = r % n_tok, q = (r / n_tok) % 4, kb = r / (4 * n_tok);
+    const uint4 v = *reinterpret_cast<const uint4 *>(x + g.x_off[k] + uint64_t(t) * g.cols[k] +
+                                                     32 * kb + 8 * q);
+    *reinterpret_cast<uint4 *>(xs + 8 * uint64_t(j)) = v;
+}
+
+template <int NB>
+struct GemmEpi {
+    static constexpr bool kSmv = false;
+    uint32_t e0, e1;    // the row block: unit elements [e0, e1)
+    const uint16_t *xk;  // the matrix's reordered activations (chunk j at xk + 8 j)
+    uint32_t cols;
+    f32x4 acc[NB];
+    uint2 pre[kGemmPre];
+    uint32_t sb0;  // row-block sub-block of pre[0]
+
+    // the lane's chunk of sub-block sb (relative to the row block)
+    __device__ __forceinline__ uint32_t chunk_at(uint32_t sb, uint32_t lane) const {
+        return e0 + 512 * sb + 8 * lane;
+    }
+
+    __device__ __forceinline__ void prefetch(const KArgs &a, uint32_t P0, uint32_t P1,
+                                             uint32_t lane) {
+        const uint32_t lo = max(P0, e0), hi = min(P1, e1);
+        sb0 = lo < hi ? (lo - e0) / 512 : 0;
+#pragma unroll
+        for (uint32_t s = 0; s < kGemmPre; s++) {
+            // sub-blocks lie wholly inside [e0, e1), so the load stays below e1
+            if (lo < hi && e0 + 512 * (sb0 + s) < hi)
+                pre[s] = *reinterpret_cast<const uint2 *>(a.sm + chunk_at(sb0 + s, lane));
+        }
+    }
+
+    template <int JP, int FMT>
+    __device__ __forceinline__ void tile(const KArgs &a, uint32_t, uint32_t P0, uint32_t P1,
+                                         uint32_t A0, uint32_t, const uint2 (&)[JP],
+                                         const uint8_t *, const uint8_t *ebuf, uint32_t lane) {
+        const uint32_t lo = max(P0, e0), hi = min(P1, e1);
+        if (lo >= hi) return;
+        const uint32_t sbA = (lo - e0) / 512, sbB = (hi - 1 - e0) / 512;
+        for (uint32_t sb = sbA; sb <= sbB; sb++) {
+            const uint32_t g = chunk_at(sb, lane);
+            uint2 S;
+            const uint32_t ps = sb - sb0;
+            if (ps < kGemmPre) {
+                S = pre[0];
+#pragma unroll
+                for (uint32_t q = 1; q < kGemmPre; q++) S = ps == q ? pre[q] : S;
+            } else {
+                S = *reinterpret_cast<const uint2 *>(a.sm + g);
+            }
+            // staged exponents of weights A0 .. P1-1; a chunk wholly outside
+            // the tile reads a clamped address and is zeroed below
+            const uint32_t ei = g < A0 ? 0u : min(g - A0, a.exp_cap - 8);
+            const uint2 E = *reinterpret_cast<const uint2 *>(ebuf + ei);
+            uint32_t w[4];
+            assemble4(S.x, E.x, w[0], w[1]);
+            assemble4(S.y, E.y, w[2], w[3]);
+            const uint32_t base = e0 + 512 * sb;
+            if (base < lo || base + 512 > hi) {  // a sub-block the tile holds in part
+#pragma unroll
+                for (uint32_t d = 0; d < 4; d++) {
+                    const uint32_t i = g + 2 * d;
+                    const uint32_t m = (i >= lo && i < hi ? 0x0000FFFFu : 0u) |
+                                       (i + 1 >= lo && i + 1 < hi ? 0xFFFF0000u : 0u);
+                    w[d] &= m;
+                }
+            }
+            bf16x8 A;
+            __builtin_memcpy(&A, w, 16);
+            // chunk (4 sb + l / 16) * T + 16 nb + l % 16 of the reordered activations
+            const uint16_t *xb = xk + 8 * ((4 * sb + (lane >> 4)) * (16 * NB) + (lane & 15u));
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+                const uint4 bv = *reinterpret_cast<const uint4 *>(xb + 8 * 16 * nb);
+                bf16x8 B;
+                __builtin_memcpy(&B, &bv, 16);
+                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[nb], 0, 0, 0);
+            }
+        }
+    }
+};
+
+// One workgroup per 16-row block (blocks of the widest matrices first, in the
+// XCD-grouped order).  The block's tiles are found in block_out_pos; each
+// wave takes every fourth.
+template <int NB>
+__global__ __launch_bounds__(kThreads) void df11_decode_gemm(KArgs a, GemmDesc g, const uint16_t *xs,
+                                                             float *y) {
+    const uint32_t mb = xcd_grouped(blockIdx.x);
+    if (mb >= g.mb0[DF11_GEMV_MAX_TENSORS]) return;  // uniform: the grid is rounded up
+    uint32_t k = 0;
+#pragma unroll
+    for (uint32_t m = 1; m <= DF11_GEMV_MAX_TENSORS; m++) k += uint32_t(mb >= g.mb0[m]);
+    const uint32_t cols = g.cols[k], rb = mb - g.mb0[k];
+    GemmEpi<NB> epi;
+    epi.e0 = g.off[k] + rb * 16 * cols;
+    epi.e1 = epi.e0 + 16 * cols;
+    epi.xk = xs + 8 * uint64_t(g.ch0[k]);
+    epi.cols = cols;
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) epi.acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    epi.sb0 = 0;
+    // tiles holding e0 and e1 - 1 (bop[0] = 0 <= e0 < e1 <= N = bop[n_tiles]
+    // for a valid unit; a corrupt bop only yields other tiles in range)
+    const uint32_t *bop = a.bop;
+    const uint32_t nt = a.n_tiles;
+    const uint32_t t0 = bop[nt] > epi.e0 ? tile_of(bop, epi.e0, 0, nt) : nt - 1;
+    const uint32_t t1 = bop[nt] > epi.e1 - 1 && bop[t0] <= epi.e1 - 1
+                            ? tile_of(bop, epi.e1 - 1, t0, nt)
+                            : nt - 1;
+    const uint32_t wid = threadIdx.x >> 6, lane = threadIdx.x & 63u;
+    const uint32_t first = min(t0, t1);
+    wave_tiles<4, DF11_FORMAT_BF16>(a, epi, first, max(t0, t1) - first + 1, wid, 4);
+
+    // ((w0 + w1) + w2) + w3 through LDS, then y^T[token][row]: lane l holds
+    // rows 4 (l / 16) .. +3 of token l % 16 of each 16-token group
+    extern __shared__ __align__(16) uint8_t dyn[];
+    f32x4 *red = reinterpret_cast<f32x4 *>(dyn);
+    __syncthreads();
+    if (wid > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) red[((wid - 1) * NB + nb) * 64 + lane] = epi.acc[nb];
+    }
+    __syncthreads();
+    if (wid == 0) {
+        const uint32_t rows = g.rows[k];
+        float *yk = y + g.y_off[k] + 16 * rb + 4 * (lane >> 4);
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            f32x4 v = epi.acc[nb];
+            v += red[(0 * NB + nb) * 64 + lane];
+            v += red[(1 * NB + nb) * 64 + lane];
+            v += red[(2 * NB + nb) * 64 + lane];
+            *reinterpret_cast<f32x4 *>(yk + uint64_t(16 * nb + (lane & 15u)) * rows) = v;
+        }
+    }
+}
+
+template <int NB>
+const void *gemm_kernel() {
+    return reinterpret_cast<const void *>(&df11_decode_gemm<NB>);
 }
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
@@ -1181,6 +1390,85 @@ int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t,
     hipLaunchKernelGGL(df11_gemv_rows, dim3((rows + kThreads - 1) / kThreads), dim3(kThreads), 0, hs,
                        d, s->block_out_pos, uint32_t(s->n_tiles), part, row_a, y);
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+}
+
+uint64_t df11_decompress_gemm_scratch_bytes(const df11_gemv_tensor *t, uint32_t n_tensors,
+                                            uint32_t n_tokens) {
+    if (!t && n_tensors) return 0;
+    uint64_t b = 0;
+    for (uint32_t k = 0; k < n_tensors; k++) b += 2ull * n_tokens * t[k].cols;
+    return b;
+}
+
+int df11_decompress_gemm(const df11_device_stream *s, const df11_gemv_tensor *t, uint32_t n_tensors,
+                         uint32_t n_tokens, const uint16_t *x, float *y, void *scratch,
+                         uint64_t scratch_bytes, int32_t *d_status, df11_hip_stream st) {
+    KArgs a{};
+    int rc = prepare(s, a);
+    if (rc != DF11_OK) return rc;
+    const uint32_t nb = n_tokens / 16;
+    if (s->format != DF11_FORMAT_BF16 || s->tile_windows != 64 || s->n_weights == 0 || !t ||
+        n_tensors == 0 || n_tensors > DF11_GEMV_MAX_TENSORS || n_tokens % 16 || nb < 1 || nb > 4 ||
+        !x || !y || !scratch || !aligned(x, 16) || !aligned(y, 16) || !aligned(scratch, 16) ||
+        scratch_bytes < df11_decompress_gemm_scratch_bytes(t, n_tensors, n_tokens))
+        return DF11_E_INVALID;
+    // widest matrices first: their row blocks take the longest
+    uint32_t order[DF11_GEMV_MAX_TENSORS];
+    for (uint32_t k = 0; k < n_tensors; k++) order[k] = k;
+    std::stable_sort(order, order + n_tensors,
+                     [t](uint32_t i, uint32_t j) { return t[i].cols > t[j].cols; });
+    GemmDesc g{};
+    g.n = n_tensors;
+    uint64_t off = 0, mbs = 0, chunks = 0;
+    for (uint32_t k = 0; k < n_tensors; k++) {
+        // in the unit the matrices follow one another in the caller's order
+        if (t[k].w_offset != off || t[k].rows == 0 || t[k].rows % 16 || t[k].cols == 0 ||
+            t[k].cols % 32 || t[k].x_offset % 8 || t[k].y_offset % 4)
+            return DF11_E_INVALID;
+        off += uint64_t(t[k].rows) * t[k].cols;
+    }
+    if (off != s->n_weights) return DF11_E_INVALID;
+    for (uint32_t i = 0; i < n_tensors; i++) {
+        const df11_gemv_tensor &d = t[order[i]];
+        if (d.x_offset >= (uint64_t(1) << 32) || d.y_offset >= (uint64_t(1) << 32))
+            return DF11_E_INVALID;
+        g.mb0[i] = uint32_t(mbs);
+        g.off[i] = uint32_t(d.w_offset);
+        g.rows[i] = d.rows;
+        g.cols[i] = d.cols;
+        g.x_off[i] = uint32_t(d.x_offset);
+        g.y_off[i] = uint32_t(d.y_offset);
+        g.ch0[i] = uint32_t(chunks);
+        mbs += d.rows / 16;
+        chunks += uint64_t(n_tokens) * d.cols / 8;
+    }
+    if (chunks >= (uint64_t(1) << 32)) return DF11_E_INVALID;
+    for (uint32_t k = n_tensors; k <= DF11_GEMV_MAX_TENSORS; k++) {
+        g.mb0[k] = uint32_t(mbs);
+        g.ch0[k] = uint32_t(chunks);
+    }
+    a.status = d_status;
+    a.out_lo = 0;
+    a.out_hi = uint32_t(s->n_weights);
+    a.n_tiles = uint32_t(s->n_tiles);
+    // the tables and four staging buffers, then (reused) three waves' sums
+    const size_t lds = std::max<size_t>(size_t(a.ebuf_off) + size_t(a.exp_cap) * 4, 3072u * nb);
+    const void *fn = nb == 1 ? gemm_kernel<1>() : nb == 2 ? gemm_kernel<2>()
+                   : nb == 3 ? gemm_kernel<3>() : gemm_kernel<4>();
+    if (lds > 65536 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+        return DF11_E_INVALID;
+    hipStream_t hs = static_cast<hipStream_t>(st);
+    uint16_t *xs = static_cast<uint16_t *>(scratch);
+    hipLaunchKernelGGL(df11_gemm_x_order, dim3(uint32_t((chunks + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, hs, g, n_tokens, x, xs);
+    if (hipGetLastError() != hipSuccess) return DF11_E_HIP;
+    const uint32_t grid = uint32_t((mbs + kXcdBlock - 1) / kXcdBlock * kXcdBlock);
+    const uint16_t *xsp = xs;
+    void *args[] = {&a, &g, &xsp, &y};
+    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, lds, hs) == hipSuccess
+               ? DF11_OK
+               : DF11_E_HIP;
 }
 
 }  // extern "C"

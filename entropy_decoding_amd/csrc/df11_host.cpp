@@ -675,4 +675,22 @@ int df11_encode(const df11_codebook *cb, const uint16_t *const *tensors, const u
                            numel, n_tensors, tile_windows, window_bytes, out);
 }
 
+int df11_gemm_order(const uint16_t *w, uint32_t rows, uint32_t cols, uint16_t *out) {
+    if (rows == 0 || cols == 0) return DF11_OK;
+    if (!w || !out || w == out || rows % 16 || cols % 32) return DF11_E_INVALID;
+    const uint32_t kbs = cols / 32;
+    // one 16-row block per task: its sub-blocks (kb) of 16 rows x 32 columns,
+    // each as four 8-column quarters q, each as 16 rows of 8 weights
+    parallel_for(rows / 16, [&](size_t m) {
+        uint16_t *o = out + m * 16 * size_t(cols);
+        for (uint32_t kb = 0; kb < kbs; kb++)
+            for (uint32_t q = 0; q < 4; q++)
+                for (uint32_t i = 0; i < 16; i++) {
+                    const uint16_t *src = w + (m * 16 + i) * size_t(cols) + 32 * kb + 8 * q;
+                    std::copy(src, src + 8, o + ((size_t(kb) * 4 + q) * 16 + i) * 8);
+                }
+    });
+    return DF11_OK;
+}
+
 }  // extern "C"

@@ -428,6 +428,49 @@ int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *te
                          uint32_t n_tensors, const float *x, float *y, void *scratch,
                          uint64_t scratch_bytes, int32_t *d_status, df11_hip_stream st);
 
+/*
+ * df11_gemm_order -- host, the weight order that df11_decompress_gemm reads:
+ * matrix w (rows x cols, row-major BF16; rows a multiple of 16, cols of 32)
+ * as 16-row blocks m in order, each as its 32-column sub-blocks kb in order,
+ * each as four 8-column quarters q, each as 16 rows i of 8 weights:
+ *   out[(((m * cols/32 + kb) * 4 + q) * 16 + i) * 8 + e] = w[(16 m + i) * cols + 32 kb + 8 q + e].
+ * A sub-block is then the A operand of one 16x16x32 matrix-core product in
+ * its lane order (lane 16 q + i holds row i, columns 8 q .. 8 q + 7), so
+ * the lanes of a wave read it contiguously.  A permutation applied before
+ * df11_build_codebook / df11_encode.  out must not overlap w.  Returns
+ * DF11_E_INVALID for other shapes or pointers.
+ */
+int df11_gemm_order(const uint16_t *w, uint32_t rows, uint32_t cols, uint16_t *out);
+
+/*
+ * df11_decompress_gemm -- device, decode fused into a matrix product on the
+ * matrix cores (the GEMM half of decoding straight into the consumer's tiles;
+ * DFloat11 decompresses right before use, abstract): for n_tokens = 16,
+ * 32, 48 or 64 tokens and each matrix k of the unit,
+ *   y[y_offset_k + t * rows_k + r] = sum over c of W_k[r][c] * x[x_offset_k + t * cols_k + c]
+ * (x: BF16 activations, token-major; y: float32, token-major), where the
+ * unit s holds every W_k in df11_gemm_order order (BF16, 64-window tiles)
+ * and tensors[k].w_offset is its offset in the unit (the matrices follow one
+ * another).  rows_k multiples of 16, cols_k of 32; x, y and scratch 16-byte
+ * aligned, x_offset_k multiples of 8, y_offset_k of 4.  scratch: at least
+ * df11_decompress_gemm_scratch_bytes(tensors, n_tensors, n_tokens) bytes
+ * (each matrix's activations reordered for the matrix cores, 2 * n_tokens *
+ * cols_k bytes); no initialisation needed.  Products are exact; sums are
+ * float32 in the matrix cores, per 16-row block each of four waves adding
+ * its 32-column sub-blocks in order, then the four waves in order
+ * (deterministic).  Weights outside a decoded tile enter as zeros, so x must
+ * be finite.  Two launches on st, no allocation; calls sharing a scratch
+ * buffer must not overlap.  Corrupt tiles are reported in *d_status as by
+ * df11_decompress_block (the rows they hold get wrong values).
+ * DF11_E_INVALID for other shapes, formats or layouts.
+ */
+uint64_t df11_decompress_gemm_scratch_bytes(const df11_gemv_tensor *tensors, uint32_t n_tensors,
+                                            uint32_t n_tokens);
+int df11_decompress_gemm(const df11_device_stream *s, const df11_gemv_tensor *tensors,
+                         uint32_t n_tensors, uint32_t n_tokens, const uint16_t *x, float *y,
+                         void *scratch, uint64_t scratch_bytes, int32_t *d_status,
+                         df11_hip_stream st);
+
 #ifdef __cplusplus
 }
 #endif

@@ -312,6 +312,24 @@ def gemv(w_flat: np.ndarray, shapes, x_flat: np.ndarray) -> np.ndarray:
     return np.concatenate(ys) if ys else np.zeros(0)
 
 
+def gemm(w_flat: np.ndarray, shapes, x_flat: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Y_k = X_k W_k^T for row-major BF16 matrices W_k stored back to back in
+    w_flat, with token-major BF16 activations X_k (n_tokens x cols_k) back to
+    back in x_flat; returns the token-major Y_k (n_tokens x rows_k) back to
+    back, float64.  Products of two BF16 values are exact in float64; sums of
+    at most 2^20 terms keep a relative error below 2^-32."""
+    w = bf16_to_f64(np.asarray(w_flat).reshape(-1))
+    x = bf16_to_f64(np.asarray(x_flat).reshape(-1))
+    ys, wo, xo = [], 0, 0
+    for rows, cols in shapes:
+        W = w[wo:wo + rows * cols].reshape(rows, cols)
+        X = x[xo:xo + n_tokens * cols].reshape(n_tokens, cols)
+        ys.append((X @ W.T).reshape(-1))
+        wo += rows * cols
+        xo += n_tokens * cols
+    return np.concatenate(ys) if ys else np.zeros(0)
+
+
 # ---------------------------------------------------------------- FP8 weights
 # (the C file's FP8 section gives the formats and the readings)
 

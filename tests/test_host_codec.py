@@ -304,3 +304,21 @@ def test_fp8_argument_errors():
     numel = (ed.ctypes.c_uint64 * 1)(b.size)
     rc = ed.LIB.df11_build_codebook_fmt(7, ptrs, numel, 1, ed.ctypes.byref(ed.df11_codebook()))
     assert rc == ed.DF11_E_INVALID
+
+
+def test_gemm_order_is_the_documented_permutation():
+    # out[(((m * cols/32 + kb) * 4 + q) * 16 + i) * 8 + e] = w[(16 m + i) * cols + 32 kb + 8 q + e]
+    rows, cols = 48, 96
+    w = np.arange(rows * cols, dtype=np.uint32).astype(np.uint16)
+    out = ed.df11_gemm_order(w, rows, cols)
+    for m, kb, q, i, e in [(0, 0, 0, 0, 0), (0, 0, 0, 1, 0), (0, 0, 1, 0, 0), (0, 1, 0, 0, 0),
+                           (1, 0, 3, 0, 7), (2, 2, 3, 15, 7), (1, 2, 2, 9, 3)]:
+        assert (out[(((m * (cols // 32) + kb) * 4 + q) * 16 + i) * 8 + e]
+                == w[(16 * m + i) * cols + 32 * kb + 8 * q + e])
+    # the same permutation by array reshapes
+    ref = w.reshape(rows // 16, 16, cols // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    assert np.array_equal(out, ref)
+    with pytest.raises(ed.Df11Error):
+        ed.df11_gemm_order(w[:40 * cols], 40, cols)  # rows not a multiple of 16
+    with pytest.raises(ed.Df11Error):
+        ed.df11_gemm_order(w[:48 * 80], 48, 80)  # cols not a multiple of 32

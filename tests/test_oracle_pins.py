@@ -377,6 +377,45 @@ def test_gemv_closed_forms_and_brute_force():
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
 
 
+def test_gemm_closed_forms_and_brute_force():
+    import struct
+
+    def bf16(v):  # the pattern as the high half of an IEEE single
+        return struct.unpack("<f", struct.pack("<I", int(v) << 16))[0]
+
+    def to_bf16(a):
+        return (np.asarray(a, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+    # ones: every output is the sum of its token's activations
+    rows, cols, n = 4, 32, 3
+    ones = np.full(rows * cols, 0x3F80, dtype=np.uint16)
+    xv = (np.arange(n * cols) % 7 - 3).astype(np.float32)
+    y = oracle.gemm(ones, [(rows, cols)], to_bf16(xv), n).reshape(n, rows)
+    assert np.array_equal(y, np.repeat(xv.reshape(n, cols).sum(1, keepdims=True), rows, 1))
+    # a selection matrix picks one activation per output row
+    sel = np.zeros((rows, cols), dtype=np.uint16)
+    sel[np.arange(rows), np.arange(rows) * 5 + 1] = 0x3F80
+    y = oracle.gemm(sel.reshape(-1), [(rows, cols)], to_bf16(xv), n).reshape(n, rows)
+    assert np.array_equal(y, xv.reshape(n, cols)[:, np.arange(rows) * 5 + 1])
+    # brute force over two matrices, token-major slices back to back
+    rng = np.random.default_rng(6)
+    shapes = [(3, 8), (2, 16)]
+    w = to_bf16(rng.standard_normal(3 * 8 + 2 * 16))
+    x = to_bf16(rng.standard_normal(n * (8 + 16)))
+    y = oracle.gemm(w, shapes, x, n)
+    ref, wo, xo = [], 0, 0
+    for r, c in shapes:
+        for t in range(n):
+            for i in range(r):
+                acc = 0.0
+                for j in range(c):
+                    acc += bf16(w[wo + i * c + j]) * bf16(x[xo + t * c + j])
+                ref.append(acc)
+        wo += r * c
+        xo += n * c
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------ FP8 weights
 
 
