@@ -1119,15 +1119,20 @@ struct GemmEpi {
             }
             bf16x8 A;
             __builtin_memcpy(&A, w, 16);
-            // chunk (4 sb + l / 16) * T + 16 nb + l % 16 of the reordered activations
+            // chunk (4 sb + l / 16) * T + 16 nb + l % 16 of the reordered activations;
+            // all NB loads are issued before the first product
             const uint16_t *xb = xk + 8 * ((4 * sb + (lane >> 4)) * (16 * NB) + (lane & 15u));
+            uint4 bv[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) bv[nb] = *reinterpret_cast<const uint4 *>(xb + 8 * 16 * nb);
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
-                const uint4 bv = *reinterpret_cast<const uint4 *>(xb + 8 * 16 * nb);
                 bf16x8 B;
-                __builtin_memcpy(&B, &bv, 16);
+                __builtin_memcpy(&B, &bv[nb], 16);
                 acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[nb], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x020, NB, 0);  // the NB vector-memory reads,
+            __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // then the NB products
         }
     }
 };
