@@ -53,6 +53,7 @@
 #include <algorithm>
 
 #include "df11.h"
+#include "df11_launch.h"
 
 namespace {
 
@@ -1392,9 +1393,11 @@ int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t,
     if (hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, lds, hs) != hipSuccess)
         return DF11_E_HIP;
     const uint32_t rows = uint32_t(row);
-    hipLaunchKernelGGL(df11_gemv_rows, dim3((rows + kThreads - 1) / kThreads), dim3(kThreads), 0, hs,
-                       d, s->block_out_pos, uint32_t(s->n_tiles), part, row_a, y);
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    return df11_detail::launch(df11_gemv_rows, dim3((rows + kThreads - 1) / kThreads),
+                               dim3(kThreads), 0, hs, d, s->block_out_pos,
+                               uint32_t(s->n_tiles), part, row_a, y) == hipSuccess
+               ? DF11_OK
+               : DF11_E_HIP;
 }
 
 uint64_t df11_decompress_gemm_scratch_bytes(const df11_gemv_tensor *t, uint32_t n_tensors,
@@ -1465,9 +1468,9 @@ int df11_decompress_gemm(const df11_device_stream *s, const df11_gemv_tensor *t,
         return DF11_E_INVALID;
     hipStream_t hs = static_cast<hipStream_t>(st);
     uint16_t *xs = static_cast<uint16_t *>(scratch);
-    hipLaunchKernelGGL(df11_gemm_x_order, dim3(uint32_t((chunks + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, hs, g, n_tokens, x, xs);
-    if (hipGetLastError() != hipSuccess) return DF11_E_HIP;
+    if (df11_detail::launch(df11_gemm_x_order, dim3(uint32_t((chunks + kThreads - 1) / kThreads)),
+                            dim3(kThreads), 0, hs, g, n_tokens, x, xs) != hipSuccess)
+        return DF11_E_HIP;
     const uint32_t grid = uint32_t((mbs + kXcdBlock - 1) / kXcdBlock * kXcdBlock);
     const uint16_t *xsp = xs;
     void *args[] = {&a, &g, &xsp, &y};

@@ -22,6 +22,7 @@
 #include <algorithm>
 
 #include "df11.h"
+#include "df11_launch.h"
 
 namespace {
 
@@ -357,9 +358,10 @@ int launch_fill(void *p, uint64_t bytes, uint32_t byte_value, hipStream_t st) {
     if (!bytes) return DF11_OK;
     const uint32_t b = byte_value * 0x01010101u;
     const uint64_t n16 = bytes / 16;
-    hipLaunchKernelGGL(enc_fill, dim3(grid_for(n16, kThreads, 4096)), dim3(kThreads), 0, st,
-                       static_cast<uint4 *>(p), n16, make_uint4(b, b, b, b));
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    return df11_detail::launch(enc_fill, dim3(grid_for(n16, kThreads, 4096)), dim3(kThreads), 0, st,
+                               static_cast<uint4 *>(p), n16, make_uint4(b, b, b, b)) == hipSuccess
+               ? DF11_OK
+               : DF11_E_HIP;
 }
 
 template <int FMT>
@@ -384,13 +386,15 @@ int encode_fmt(const df11_codebook *cb, const void *w, uint64_t n, const df11_si
         rc = launch_fill(o->sm + sm_done, sz->sm_bytes - sm_done, 0, st);
     if (rc == DF11_OK) rc = launch_fill(o->d_max_tile_symbols, 16, 0, st);
     if (rc != DF11_OK) return rc;
-    hipLaunchKernelGGL(enc_group_bits<FMT>, dim3(uint32_t(groups)), dim3(kThreads), 0, st, w, n, c,
-                       group_bits);
-    hipLaunchKernelGGL(enc_run_sums, dim3(runs), dim3(kScanRun), 0, st, group_bits, uint32_t(groups),
-                       run_sum);
-    hipLaunchKernelGGL(enc_scan_runs, dim3(1), dim3(kScanRun), 0, st, run_sum, runs);
-    hipLaunchKernelGGL(enc_scan_within, dim3(runs), dim3(kScanRun), 0, st, group_bits,
-                       uint32_t(groups), run_sum, start);
+    using df11_detail::launch;
+    if (launch(enc_group_bits<FMT>, dim3(uint32_t(groups)), dim3(kThreads), 0, st, w, n, c,
+               group_bits) != hipSuccess ||
+        launch(enc_run_sums, dim3(runs), dim3(kScanRun), 0, st, group_bits, uint32_t(groups),
+               run_sum) != hipSuccess ||
+        launch(enc_scan_runs, dim3(1), dim3(kScanRun), 0, st, run_sum, runs) != hipSuccess ||
+        launch(enc_scan_within, dim3(runs), dim3(kScanRun), 0, st, group_bits, uint32_t(groups),
+               run_sum, start) != hipSuccess)
+        return DF11_E_HIP;
     EmitArgs a{};
     a.w = w;
     a.n = n;
@@ -410,10 +414,11 @@ int encode_fmt(const df11_codebook *cb, const void *w, uint64_t n, const df11_si
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(&enc_emit<FMT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
         return DF11_E_HIP;
-    hipLaunchKernelGGL(enc_emit<FMT>, dim3(uint32_t(groups)), dim3(kThreads), lds, st, a);
-    hipLaunchKernelGGL(enc_max_tile, dim3(grid_for(sz->n_tiles, kThreads, 1024)), dim3(kThreads), 0,
-                       st, o->block_out_pos, uint32_t(sz->n_tiles), o->d_max_tile_symbols);
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    if (launch(enc_emit<FMT>, dim3(uint32_t(groups)), dim3(kThreads), lds, st, a) != hipSuccess ||
+        launch(enc_max_tile, dim3(grid_for(sz->n_tiles, kThreads, 1024)), dim3(kThreads), 0, st,
+               o->block_out_pos, uint32_t(sz->n_tiles), o->d_max_tile_symbols) != hipSuccess)
+        return DF11_E_HIP;
+    return DF11_OK;
 }
 
 }  // namespace
@@ -430,13 +435,12 @@ int df11_histogram_device(uint32_t format, const void *w, uint64_t n, uint64_t *
     if (rc != DF11_OK || n == 0) return rc;
     const uint32_t grid = grid_for(n, uint64_t(kThreads) * 16 * 8, 4096);
     auto *c = reinterpret_cast<unsigned long long *>(d_counts);
-    if (format == DF11_FORMAT_BF16)
-        hipLaunchKernelGGL(enc_histogram<DF11_FORMAT_BF16>, dim3(grid), dim3(kThreads), 0, st, w, n, c);
-    else if (format == DF11_FORMAT_FP8_E4M3)
-        hipLaunchKernelGGL(enc_histogram<DF11_FORMAT_FP8_E4M3>, dim3(grid), dim3(kThreads), 0, st, w, n, c);
-    else
-        hipLaunchKernelGGL(enc_histogram<DF11_FORMAT_FP8_E5M2>, dim3(grid), dim3(kThreads), 0, st, w, n, c);
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_E_HIP;
+    auto *k = format == DF11_FORMAT_BF16       ? enc_histogram<DF11_FORMAT_BF16>
+              : format == DF11_FORMAT_FP8_E4M3 ? enc_histogram<DF11_FORMAT_FP8_E4M3>
+                                               : enc_histogram<DF11_FORMAT_FP8_E5M2>;
+    return df11_detail::launch(k, dim3(grid), dim3(kThreads), 0, st, w, n, c) == hipSuccess
+               ? DF11_OK
+               : DF11_E_HIP;
 }
 
 uint64_t df11_encode_device_scratch_bytes(uint64_t n_weights) {

@@ -415,7 +415,8 @@ int df11_gemv_bf16(const uint16_t *w, const df11_gemv_tensor *tensors, uint32_t 
  * otherwise): a BF16 unit with 64-window tiles; the tensors tile the unit in
  * order (w_offset_k = sum of the previous rows * cols), cols_k multiples of 8,
  * x 16-byte aligned with x_offset_k multiples of 4; no tile may touch more
- * than 4 rows, i.e. (max_tile_symbols - 1) / min_k cols_k + 2 <= 4.  Each
+ * than 4 rows, i.e. (max_tile_symbols - 1) / min_k cols_k + 2 <= 4; x, y and
+ * scratch must not overlap.  Each
  * output is a sum formed in a fixed order: per weight chunk of 8 a chain of
  * fused multiply-adds, per lane the chunks in order, a butterfly over the
  * wave, then per row the tiles in order (deterministic; it differs from
@@ -452,7 +453,7 @@ int df11_gemm_order(const uint16_t *w, uint32_t rows, uint32_t cols, uint16_t *o
  * unit s holds every W_k in df11_gemm_order order (BF16, 64-window tiles)
  * and tensors[k].w_offset is its offset in the unit (the matrices follow one
  * another).  rows_k multiples of 16, cols_k of 32; x, y and scratch 16-byte
- * aligned, x_offset_k multiples of 8, y_offset_k of 4.  scratch: at least
+ * aligned and not overlapping, x_offset_k multiples of 8, y_offset_k of 4.  scratch: at least
  * df11_decompress_gemm_scratch_bytes(tensors, n_tensors, n_tokens) bytes
  * (each matrix's activations reordered for the matrix cores, 2 * n_tokens *
  * cols_k bytes); no initialisation needed.  Products are exact; sums are
