@@ -939,7 +939,7 @@ struct GemvEpi {
     }
 };
 
-__global__ __launch_bounds__(kThreads, 7) void df11_decode_gemv(KArgs a, GemvDesc d, const float *x,
+__global__ __launch_bounds__(kThreads, 8) void df11_decode_gemv(KArgs a, GemvDesc d, const float *x,
                                                              float *part, uint32_t *row_a) {
     GemvEpi epi{&d, x, part, row_a};
     wave_tiles<4, DF11_FORMAT_BF16>(a, epi);
@@ -1247,8 +1247,10 @@ int prepare(const df11_device_stream *s, KArgs &a) {
     // none, so that a walk on corrupt input still reads inside the allocation
     a.lut_last = s->n_luts > 1 ? s->n_luts - 1 : 1u;
     a.lds_tables = kLutOff + 512u * (s->n_luts - 1);
-    // dynamic LDS: hierarchical tables, 16 bytes of wave totals, staging
-    a.ebuf_off = 512u * a.lut_last + 16;
+    // dynamic LDS: hierarchical tables, 16 bytes of wave totals (workgroup
+    // tiles only), staging.  With 64-window tiles a Llama block then needs
+    // 20,480 bytes per workgroup in all, so 8 workgroups fit in a CU's 160 KiB
+    a.ebuf_off = 512u * a.lut_last + (s->tile_windows == 64 ? 0u : 16u);
     // outputs from P0 rounded down to a chunk to the last chunk, plus the 2 spill bytes
     const uint32_t chunk = chunk_outputs(s->format);
     a.exp_cap = (s->max_tile_symbols + (chunk - 1) + 16 + 15) & ~15u;
