@@ -322,3 +322,20 @@ def test_gemm_order_is_the_documented_permutation():
         ed.df11_gemm_order(w[:40 * cols], 40, cols)  # rows not a multiple of 16
     with pytest.raises(ed.Df11Error):
         ed.df11_gemm_order(w[:48 * 80], 48, 80)  # cols not a multiple of 32
+
+
+def test_fused_workspace_sizes():
+    """Host-only size queries of the fused entry points (no device call)."""
+    shapes = [(64, 1024), (32, 4096)]
+    lay = ed.gemm_layout(shapes, 48)
+    assert ed.df11_decompress_gemm_scratch_bytes(lay, 48) == 2 * 48 * (1024 + 4096)
+    assert ed.LIB.df11_decompress_gemm_scratch_bytes(None, 0, 16) == 0
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal(64 * 1024).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    cb = ed.df11_build_codebook([w])
+    hs = ed.df11_encode(cb, [w], 64, 8)
+    desc = ed.df11_device_stream()
+    desc.n_tiles = hs.n_tiles
+    # four row sums and a first-row index per tile, plus alignment slack
+    assert ed.LIB.df11_decompress_gemv_scratch_bytes(ed.ctypes.byref(desc)) == hs.n_tiles * 20 + 256
+    assert ed.LIB.df11_decompress_gemv_scratch_bytes(None) == 0
