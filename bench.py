@@ -459,6 +459,10 @@ def encode_bench(args, torch, ed, sw):
              and int(bufs[4][:4].cpu().numpy().view(np.uint32)[0]) == hs.max_tile_symbols)
     total_ms = float(h_ms.mean() + e_ms.mean())
     in_bytes = n * (2 if fmt == "bf16" else 1)
+    # the encode call (the larger share): weights read once, compressed arrays
+    # (stream, sign+mantissa, gaps, block_out_pos) written once
+    enc_alg = in_bytes + (hs.total_bits + 7) // 8 + hs.sm.size + hs.gaps.size + 4 * hs.block_out_pos.size
+    enc_ach = enc_alg / (float(e_ms.mean()) * 1e-3) / 1e9
     line = {
         "metric": "GPU encode GB/s (input weights)", "value": round(in_bytes / (total_ms * 1e-3) / 1e9, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "higher_is_better": True,
@@ -468,6 +472,9 @@ def encode_bench(args, torch, ed, sw):
         "device_ms": {"histogram": round(float(h_ms.mean()), 4), "encode": round(float(e_ms.mean()), 4),
                       "codebook_on_host": round(codebook_ms, 3)},
         "host_encoder_ms": round(host_ms, 1),
+        "roofline": {"bound": "hbm", "achieved": round(enc_ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(enc_ach / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": int(enc_alg), "kernel": "df11_encode_device (all launches)"},
     }
     print(json.dumps(line), flush=True)
     if not exact:
