@@ -339,3 +339,38 @@ def test_fused_workspace_sizes():
     # four row sums and a first-row index per tile, plus alignment slack
     assert ed.LIB.df11_decompress_gemv_scratch_bytes(ed.ctypes.byref(desc)) == hs.n_tiles * 20 + 256
     assert ed.LIB.df11_decompress_gemv_scratch_bytes(None) == 0
+
+
+def test_random_units_match_oracle_property():
+    """Generated units (sizes, tensor splits, value spreads, raw bit patterns,
+    few-exponent data, tile sizes): the library's codebook, stream and
+    auxiliary arrays equal the oracle's byte for byte."""
+    from hypothesis import HealthCheck, given, settings
+    from hypothesis import strategies as st
+
+    @settings(max_examples=60, deadline=None, derandomize=True,
+              suppress_health_check=[HealthCheck.too_slow])
+    @given(data=st.data())
+    def check(data):
+        rng = np.random.default_rng(data.draw(st.integers(0, 2 ** 32 - 1), label="seed"))
+        mode = data.draw(st.sampled_from(["gauss", "bits", "few"]), label="mode")
+        tensors = []
+        for _ in range(data.draw(st.integers(1, 4), label="tensors")):
+            n = data.draw(st.integers(0, 6000), label="numel")
+            if mode == "gauss":
+                sigma = data.draw(st.sampled_from([1e-3, 0.02, 1.0, 300.0]), label="sigma")
+                v = (rng.standard_normal(n) * sigma).astype(np.float32)
+                t = ((v.view(np.uint32) + 0x7FFF + ((v.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+            elif mode == "bits":
+                t = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
+            else:
+                exps = rng.choice(256, size=int(rng.integers(1, 4)), replace=False)
+                t = ((rng.choice(exps, n).astype(np.uint32) << 7)
+                     | rng.integers(0, 128, n).astype(np.uint32)
+                     | (rng.integers(0, 2, n).astype(np.uint32) << 15)).astype(np.uint16)
+            tensors.append(t)
+        if sum(t.size for t in tensors) == 0:
+            tensors.append(np.array([0x3F80], dtype=np.uint16))
+        _compare(tensors, data.draw(st.sampled_from([64, 256, 512]), label="tile windows"), 8)
+
+    check()
