@@ -191,135 +191,141 @@ struct Windows {
 };
 
 // Phase 1: cnt[c] = number of codes whose first bit lies in [gap_c, lim_c).
+// A step adds every code start that its count-table entry marks in the 12
+// bits it looks at; only a chain's last step can reach past lim, so the
+// starts at or after lim are taken off once, after the loops, from that
+// step's entry (kept in el: finished chains are masked off and keep it).
 template <int C>
 __device__ __forceinline__ void count_codes(const Windows<C> &W, const uint32_t (&gap)[C],
                                             const uint32_t (&lim)[C], const uint8_t *fast,
                                             const uint16_t *lut, uint32_t last,
                                             uint32_t (&cnt)[C]) {
-    uint32_t q[C], bad[C];
+    uint32_t q[C], bad[C], el[C];
 #pragma unroll
     for (int c = 0; c < C; c++) {
         q[c] = ~gap[c];
         cnt[c] = 0;
         bad[c] = 0;
+        el[c] = 0;
     }
 #pragma unroll
     for (int s = 0; s < 2; s++) {
         uint32_t qend[C];
 #pragma unroll
         for (int c = 0; c < C; c++) qend[c] = ~min(32u * (s + 1), lim[c]);  // p < end <=> q > ~end
-        for (;;) {
-            bool act[C];
-            uint64_t am[C], any = 0;
-#pragma unroll
-            for (int c = 0; c < C; c++) {
-                act[c] = q[c] > qend[c];
-                am[c] = ballot(act[c]);
-                any |= am[c];
+        // one step of chain c
+        auto step = [&](int c) {
+            const uint32_t w32 = W.at(c, s, q[c]);
+            uint32_t e = *reinterpret_cast<const uint16_t *>(
+                fast + kCountOff + ((w32 >> (32 - DF11_COUNT_BITS)) << 1));
+            if (__builtin_expect(e < (1u << 12), 0)) {  // rare: a first code longer than the index
+                const uint32_t len = walk_tables(lut, last, e, w32, true) >> 8;
+                // one code of that length; none at all means a corrupt input
+                bad[c] |= len ? 0u : kBadCount;
+                e = len ? (len << 12) | 1u : (64u << 12);
             }
-            if (!any) break;
-            uint32_t w32[C], e[C];
-            uint64_t longc = 0;
-#pragma unroll
-            for (int c = 0; c < C; c++) {
-                w32[c] = W.at(c, s, q[c]);
-                e[c] = *reinterpret_cast<const uint16_t *>(
-                    fast + kCountOff + ((w32[c] >> (32 - DF11_COUNT_BITS)) << 1));
-                longc |= ballot(e[c] < (1u << 12)) & am[c];
-            }
-            if (longc) {  // rare: a first code longer than the count index
+            cnt[c] += uint32_t(__builtin_popcount(e & 0xFFFu));
+            q[c] -= e >> 12;
+            el[c] = e;
+        };
+        // divergent loops: a lane leaves (is masked off) when its chains are done
+        if constexpr (C == 1) {
+            while (q[0] > qend[0]) step(0);
+        } else {
+            for (;;) {
+                bool act[C], any = false;
 #pragma unroll
                 for (int c = 0; c < C; c++) {
-                    if (act[c] && (e[c] >> 12) == 0) {
-                        const uint32_t len = walk_tables(lut, last, e[c] & 0xFFFu, w32[c], true) >> 8;
-                        // one code of that length; none at all means a corrupt input
-                        e[c] = len ? (len << 12) | 1u : (64u << 12);
-                        bad[c] |= len ? 0u : kBadCount;
-                    }
+                    act[c] = q[c] > qend[c];
+                    any |= act[c];
                 }
-            }
-            // finished chains are masked off: they count nothing and do not move
+                if (!any) break;
 #pragma unroll
-            for (int c = 0; c < C; c++) {
-                if (act[c]) {
-                    // only starts before lim count (lim - p == lim + 1 + q)
-                    const uint32_t cut = min(lim[c] + 1 + q[c], uint32_t(DF11_COUNT_BITS));
-                    cnt[c] += uint32_t(__builtin_popcount(__builtin_amdgcn_ubfe(e[c], 0, cut)));
-                    q[c] -= e[c] >> 12;
-                }
+                for (int c = 0; c < C; c++)
+                    if (act[c]) step(c);
             }
         }
     }
 #pragma unroll
-    for (int c = 0; c < C; c++) cnt[c] += bad[c];
+    for (int c = 0; c < C; c++) {
+        // the last step started at p_last = p - advance; starts at offset
+        // >= lim - p_last in its mask lie at or beyond lim
+        const uint32_t cut = min(lim[c] - (~q[c] - (el[c] >> 12)), uint32_t(DF11_COUNT_BITS));
+        cnt[c] -= uint32_t(__builtin_popcount(__builtin_amdgcn_ubfe(el[c], cut, DF11_COUNT_BITS - cut)));
+        cnt[c] += bad[c];
+    }
+}
+
+// One phase-2 step of a chain: the multi-symbol entry at its position (a
+// long first code resolved), its three exponent bytes written at dst, dst
+// and q advanced.  Returns the entry.  Called in divergent code: only the
+// lanes whose chain takes the step run it.
+__device__ __forceinline__ uint32_t decode_step(uint32_t w32, const uint8_t *fast,
+                                                const uint16_t *lut, uint32_t last,
+                                                uint32_t &dst, uint32_t &q) {
+    uint32_t e = *reinterpret_cast<const uint32_t *>(
+        fast + kMultiOff + ((w32 >> (32 - DF11_MULTI_BITS)) << 2));
+    if (__builtin_expect(e < (1u << 30), 0))  // rare: a first code longer than 10 bits
+        e = long_entry(lut, last, e, w32, true);
+    lds8 *o = (lds8 *)size_t(dst);
+    o[0] = uint8_t(e);
+    o[1] = uint8_t(e >> 8);
+    o[2] = uint8_t(e >> 16);
+    dst += e >> 30;
+    q -= (e >> 24) & 0x3Fu;
+    return e;
 }
 
 // Phase 2: exponents of window c's codes to LDS bytes dst[c] .., up to 2
 // bytes beyond.  dst are LDS addresses, so the stores need no base added.
+// A window's last step may write up to two bytes past its codes, onto the
+// next window's first two outputs; f01[c] returns window c's own first two
+// exponents (byte 0 and byte 1) for rewriting those afterwards.  The first
+// two steps are taken at any position below lim (they can cross into the
+// second 32-bit segment); the loops then run segment by segment.  Lanes
+// whose chains are done are masked off: they neither write nor move.
 template <int C>
 __device__ __forceinline__ void decode_codes(const Windows<C> &W, const uint32_t (&gap)[C],
                                              const uint32_t (&lim)[C], const uint8_t *fast,
                                              const uint16_t *lut, uint32_t last,
-                                             uint32_t (&dst)[C]) {
+                                             uint32_t (&dst)[C], uint32_t (&f01)[C]) {
     uint32_t q[C];
 #pragma unroll
-    for (int c = 0; c < C; c++) q[c] = ~gap[c];
+    for (int c = 0; c < C; c++) {
+        q[c] = ~gap[c];
+        f01[c] = 0;
+        if (q[c] > ~lim[c]) f01[c] = decode_step(W.at_low(c, ~q[c]), fast, lut, last, dst[c], q[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        if (q[c] > ~lim[c]) {
+            const uint32_t e = decode_step(W.at_low(c, ~q[c]), fast, lut, last, dst[c], q[c]);
+            // the second exponent is the first entry's second symbol when it holds two or more
+            if ((f01[c] >> 30) < 2) f01[c] = __builtin_amdgcn_perm(e, f01[c], 0x07070400u);
+        }
+    }
 #pragma unroll
     for (int s = 0; s < 2; s++) {
         uint32_t qend[C];
 #pragma unroll
         for (int c = 0; c < C; c++) qend[c] = ~min(32u * (s + 1), lim[c]);
-        for (;;) {
-            bool act[C];
-            uint64_t am[C], any = 0;
-#pragma unroll
-            for (int c = 0; c < C; c++) {
-                act[c] = q[c] > qend[c];
-                am[c] = ballot(act[c]);
-                any |= am[c];
-            }
-            if (!any) break;
-            uint32_t w32[C], e[C];
-            uint64_t longc = 0;
-#pragma unroll
-            for (int c = 0; c < C; c++) {
-                w32[c] = W.at(c, s, q[c]);
-                e[c] = *reinterpret_cast<const uint32_t *>(
-                    fast + kMultiOff + ((w32[c] >> (32 - DF11_MULTI_BITS)) << 2));
-                longc |= ballot(e[c] < (1u << 30)) & am[c];
-            }
-            if (longc) {  // rare: a first code longer than 10 bits
+        if constexpr (C == 1) {
+            while (q[0] > qend[0]) decode_step(W.at(0, s, q[0]), fast, lut, last, dst[0], q[0]);
+        } else {
+            for (;;) {
+                bool act[C], any = false;
 #pragma unroll
                 for (int c = 0; c < C; c++) {
-                    const uint32_t le = long_entry(lut, last, e[c], w32[c], act[c] && e[c] < (1u << 30));
-                    e[c] = e[c] < (1u << 30) ? le : e[c];
+                    act[c] = q[c] > qend[c];
+                    any |= act[c];
                 }
-            }
-            // finished chains are masked off: they neither write nor move
+                if (!any) break;
 #pragma unroll
-            for (int c = 0; c < C; c++) {
-                if (act[c]) {
-                    lds8 *o = (lds8 *)size_t(dst[c]);
-                    o[0] = uint8_t(e[c]);
-                    o[1] = uint8_t(e[c] >> 8);
-                    o[2] = uint8_t(e[c] >> 16);
-                    dst[c] += e[c] >> 30;
-                    q[c] -= (e[c] >> 24) & 0x3Fu;
-                }
+                for (int c = 0; c < C; c++)
+                    if (act[c]) decode_step(W.at(c, s, q[c]), fast, lut, last, dst[c], q[c]);
             }
         }
     }
-}
-
-// The multi-symbol entry at bit p (< 64) of window c, long codes resolved.
-template <int C>
-__device__ __forceinline__ uint32_t entry_at(const Windows<C> &W, int c, uint32_t p,
-                                             const uint8_t *fast, const uint16_t *lut,
-                                             uint32_t last) {
-    const uint32_t w32 = W.at_low(c, p);
-    const uint32_t e = *reinterpret_cast<const uint32_t *>(
-        fast + kMultiOff + ((w32 >> (32 - DF11_MULTI_BITS)) << 2));
-    return e < (1u << 30) ? long_entry(lut, last, e, w32, true) : e;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -459,22 +465,14 @@ __global__ __launch_bounds__(kThreads) void df11_decode(KArgs a) {
         for (int c = 1; c < C; c++) first[c] = first[c - 1] + cnt[c - 1];
 #pragma unroll
         for (int c = 0; c < C; c++) dst[c] = first[c];
-        decode_codes<C>(win, gap, lim, fast, lut, a.lut_last, dst);
+        uint32_t f01[C];
+        decode_codes<C>(win, gap, lim, fast, lut, a.lut_last, dst, f01);
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < C; c++) {
-            if (cnt[c]) {
-                uint32_t e = entry_at<C>(win, c, gap[c], fast, lut, a.lut_last);
-                lds8 *o = (lds8 *)size_t(first[c]);
-                o[0] = uint8_t(e);
-                if (cnt[c] > 1) {
-                    if ((e >> 30) < 2)
-                        e = entry_at<C>(win, c, gap[c] + ((e >> 24) & 0x3Fu), fast, lut, a.lut_last);
-                    else
-                        e >>= 8;
-                    o[1] = uint8_t(e);
-                }
-            }
+            lds8 *o = (lds8 *)size_t(first[c]);
+            if (cnt[c]) o[0] = uint8_t(f01[c]);
+            if (cnt[c] > 1) o[1] = uint8_t(f01[c] >> 8);
         }
         __syncthreads();
 
@@ -651,21 +649,15 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi, uint32_t fi
         uint32_t first[1], dst[1];
         first[0] = lds_addr(ebuf) + (P0 - A0) + incl - cnt[0];
         dst[0] = first[0];
-        decode_codes<1>(win, gap, lim, fast, lut, a.lut_last, dst);
+        uint32_t f01[1];
+        decode_codes<1>(win, gap, lim, fast, lut, a.lut_last, dst, f01);
         // keep the compiler from moving LDS accesses across the steps below;
         // the hardware keeps one wave's LDS operations in order
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (cnt[0]) {
-            uint32_t e = entry_at<1>(win, 0, gap[0], fast, lut, a.lut_last);
+        {
             lds8 *o = (lds8 *)size_t(first[0]);
-            o[0] = uint8_t(e);
-            if (cnt[0] > 1) {
-                if ((e >> 30) < 2)
-                    e = entry_at<1>(win, 0, gap[0] + ((e >> 24) & 0x3Fu), fast, lut, a.lut_last);
-                else
-                    e >>= 8;
-                o[1] = uint8_t(e);
-            }
+            if (cnt[0]) o[0] = uint8_t(f01[0]);
+            if (cnt[0] > 1) o[1] = uint8_t(f01[0] >> 8);
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
