@@ -143,15 +143,17 @@ struct TileIn {
     uint32_t gaps;  // gap of window c in byte c
     uint32_t bounds;
     // t: the thread's index among the tile's W / C threads
+    // (tile is wave-uniform: the tile's base addresses stay scalar)
     template <uint32_t W>
     __device__ __forceinline__ void load(const KArgs &a, uint32_t tile, uint32_t t) {
-        const uint64_t win0 = uint64_t(tile) * W + uint64_t(C) * t;
-        const uint8_t *wp = a.stream + win0 * 8;
+        const uint64_t win0 = uint64_t(tile) * W;
+        const uint8_t *wp = a.stream + win0 * 8 + 8 * C * t;
+        const uint8_t *gp = a.gaps + win0 + C * t;
         if constexpr (C == 1) {
             const uint2 v = *reinterpret_cast<const uint2 *>(wp);
             d[0] = v.x;
             d[1] = v.y;
-            gaps = a.gaps[win0];
+            gaps = *gp;
         } else {
             static_assert(C == 2, "one or two windows per thread");
             const uint4 v = *reinterpret_cast<const uint4 *>(wp);
@@ -159,10 +161,10 @@ struct TileIn {
             d[1] = v.y;
             d[2] = v.z;
             d[3] = v.w;
-            gaps = *reinterpret_cast<const uint16_t *>(a.gaps + win0);
+            gaps = *reinterpret_cast<const uint16_t *>(gp);
         }
         d[2 * C] = *reinterpret_cast<const uint32_t *>(wp + 8 * C);
-        bounds = a.bop[tile + (t & 1u)];
+        bounds = (a.bop + tile)[t & 1u];
     }
 };
 
@@ -504,6 +506,16 @@ struct OutFmt<DF11_FORMAT_BF16> {
                                                  const uint8_t *ex) {
         store8(a, gi, s8, ex);
     }
+    // chunk c counted from output element base (which may lie before out)
+    static __device__ __forceinline__ void store_at(const KArgs &a, int64_t base, uint32_t c,
+                                                    uint2 s8, const uint8_t *ex) {
+        const uint2 e8 = *reinterpret_cast<const uint2 *>(ex);
+        uint4 v;
+        assemble4(s8.x, e8.x, v.x, v.y);
+        assemble4(s8.y, e8.y, v.z, v.w);
+        uint16_t *o = static_cast<uint16_t *>(a.out) + base;
+        reinterpret_cast<uint4 *>(o)[c] = v;
+    }
     // element k (< 8) of a chunk
     static __device__ __forceinline__ void store1(const KArgs &a, uint32_t i, uint2 s8, uint32_t k,
                                                   uint32_t e) {
@@ -526,15 +538,23 @@ struct OutFp8 {
         const uint32_t u = __builtin_amdgcn_perm(S, S, sel);
         return (u & 0x000F000Fu) | ((u >> 4) & 0x0F000F00u);
     }
-    static __device__ __forceinline__ void store(const KArgs &a, uint32_t gi, uint2 s8,
-                                                 const uint8_t *ex) {
+    static __device__ __forceinline__ uint4 chunk(uint2 s8, const uint8_t *ex) {
         const uint4 e16 = *reinterpret_cast<const uint4 *>(ex);
         uint4 v;
         v.x = assemble(spread(s8.x, 0x01010000u), e16.x);
         v.y = assemble(spread(s8.x, 0x03030202u), e16.y);
         v.z = assemble(spread(s8.y, 0x01010000u), e16.z);
         v.w = assemble(spread(s8.y, 0x03030202u), e16.w);
-        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.out) + (gi - a.out_shift)) = v;
+        return v;
+    }
+    static __device__ __forceinline__ void store(const KArgs &a, uint32_t gi, uint2 s8,
+                                                 const uint8_t *ex) {
+        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.out) + (gi - a.out_shift)) = chunk(s8, ex);
+    }
+    static __device__ __forceinline__ void store_at(const KArgs &a, int64_t base, uint32_t c,
+                                                    uint2 s8, const uint8_t *ex) {
+        uint8_t *o = static_cast<uint8_t *>(a.out) + base;
+        reinterpret_cast<uint4 *>(o)[c] = chunk(s8, ex);
     }
     static __device__ __forceinline__ void store1(const KArgs &a, uint32_t i, uint2 s8, uint32_t k,
                                                   uint32_t e) {
@@ -617,7 +637,7 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi, uint32_t fi
 #pragma unroll
             for (int j = 0; j < JP; j++) {
                 const uint32_t c = lane + j * 64;
-                if (c < n8) smv[j] = *reinterpret_cast<const uint2 *>(sm0 + 8 * c);
+                if (c < n8) smv[j] = reinterpret_cast<const uint2 *>(sm0 + 8 * size_t(lane))[64 * j];
             }
         }
         if (sane) epi.prefetch(a, P0, P1, lane);
@@ -632,8 +652,10 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi, uint32_t fi
         uint32_t gap[1], lim[1];
         gap[0] = cur.gaps & 0xFFu;
         {
-            const uint64_t base = (uint64_t(tile) * W + lane) * 64;
-            lim[0] = a.total_bits > base ? uint32_t(min<uint64_t>(64, a.total_bits - base)) : 0u;
+            // stream bits of the tile (uniform), then this lane's share of them
+            const uint64_t tbase = uint64_t(tile) * W * 64;
+            const uint32_t rem = a.total_bits > tbase ? uint32_t(min<uint64_t>(W * 64, a.total_bits - tbase)) : 0u;
+            lim[0] = uint32_t(min(max(int32_t(rem) - int32_t(64 * lane), 0), 64));
         }
 
         uint32_t cnt[1];
@@ -675,18 +697,21 @@ struct StoreEpi {
                                          const uint8_t *sm0, const uint8_t *ebuf, uint32_t lane) {
         using F = OutFmt<FMT>;
         constexpr uint32_t CH = F::kChunk;
-        // whole chunks: the lanes of the wave write 1 KiB contiguously per j
+        // whole chunks: the lanes of the wave write 1 KiB contiguously per j.
+        // Chunk c is whole and in range when c_lo <= c < c_hi (uniform bounds).
         const uint32_t lo = max(P0, a.out_lo), hi = min(P1, a.out_hi);
+        const int32_t c_lo = int32_t((lo - A0 + CH - 1) / CH);
+        const int32_t c_hi = hi > A0 ? int32_t((hi - A0) / CH) : 0;
+        const int32_t r0 = int32_t(lane) - c_lo, r1 = int32_t(lane) - c_hi;
+        const uint8_t *el = ebuf + CH * lane;
+        const int64_t base = int64_t(A0) - int64_t(a.out_shift);  // output index of chunk 0
 #pragma unroll
-        for (int j = 0; j < JP; j++) {
-            const uint32_t c = lane + j * 64;
-            const uint32_t gi = A0 + CH * c;
-            if (c < n8 && gi >= lo && gi + CH <= hi) F::store(a, gi, smv[j], ebuf + CH * c);
-        }
+        for (int j = 0; j < JP; j++)
+            if (r0 >= -64 * j && r1 < -64 * j)
+                F::store_at(a, base, lane + 64 * j, smv[j], el + 64 * CH * j);
         for (uint32_t c = lane + JP * 64; c < n8; c += 64) {
-            const uint32_t gi = A0 + CH * c;
-            if (gi >= lo && gi + CH <= hi)
-                F::store(a, gi, *reinterpret_cast<const uint2 *>(sm0 + 8 * c), ebuf + CH * c);
+            if (int32_t(c) >= c_lo && int32_t(c) < c_hi)
+                F::store_at(a, base, c, *reinterpret_cast<const uint2 *>(sm0 + 8 * c), ebuf + CH * c);
         }
         // the chunks holding the first and last output in range, element by
         // element: lanes 0 .. CH-1 and CH .. 2CH-1 (they are whole only when aligned)
@@ -707,7 +732,7 @@ struct StoreEpi {
 // XCD-grouped order
 template <int JP, int FMT, class Epi>
 __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi) {
-    const uint32_t wid = threadIdx.x >> 6;
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
     wave_tiles<JP, FMT>(a, epi, a.tile0, a.n_tiles, 4 * xcd_grouped(blockIdx.x) + wid,
                         4 * gridDim.x);
 }
@@ -1195,9 +1220,9 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 const void *kernel_for(uint32_t tile_windows, uint32_t format) {
     if (format == DF11_FORMAT_FP8_E4M3)
-        return reinterpret_cast<const void *>(&df11_decode_wave<4, DF11_FORMAT_FP8_E4M3>);
+        return reinterpret_cast<const void *>(&df11_decode_wave<2, DF11_FORMAT_FP8_E4M3>);
     if (format == DF11_FORMAT_FP8_E5M2)
-        return reinterpret_cast<const void *>(&df11_decode_wave<4, DF11_FORMAT_FP8_E5M2>);
+        return reinterpret_cast<const void *>(&df11_decode_wave<2, DF11_FORMAT_FP8_E5M2>);
     if (tile_windows == 64)
         return reinterpret_cast<const void *>(&df11_decode_wave<4, DF11_FORMAT_BF16>);
     return tile_windows == 256 ? reinterpret_cast<const void *>(&df11_decode<1, 4>)
