@@ -119,14 +119,44 @@ def test_fp8_random_multi_tensor_units(seed):
         assert np.array_equal(out[: t.size].cpu().numpy(), t)
 
 
-def test_fp8_corrupt_block_out_pos_is_reported(unit_tensors):
+def test_fp8_corrupt_block_out_pos_is_reported_and_tiles_left_unwritten(unit_tensors):
     (w,) = unit_tensors("0")
-    u = Unit([_fp8(w, "fp8_e4m3")], "fp8_e4m3")
-    bad = u.hs.block_out_pos.copy()
-    bad[9] += 1
+    b = _fp8(w, "fp8_e4m3")
+    u = Unit([b], "fp8_e4m3")
+    bop = u.hs.block_out_pos.copy()
+    bad = bop.copy()
+    bad[9] += 1  # tiles 8 and 9 now disagree with their decoded counts
     u.ds.block_out_pos.copy_(torch.from_numpy(bad.view(np.uint8)))
-    _, st = u.decompress(0xA5, "corrupt bop")
+    out, st = u.decompress(0xA5, "corrupt bop")
     assert st == ed.DF11_E_CORRUPT
+    got = out.cpu().numpy()
+    # tiles 8, 9 wrote nothing (away from the chunks they share with 7 and 10);
+    # every other tile is exact
+    lo, hi = int(bad[8]), int(bad[10])
+    assert (got[lo + 16:hi - 16] == 0xA5).all()
+    assert np.array_equal(got[: int(bop[8])], b[: int(bop[8])])
+    assert np.array_equal(got[int(bop[10]):], b[int(bop[10]):])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_long_tiles_take_the_general_store_path(fmt):
+    # Nearly every weight shares one exponent: codes of about one bit, so a
+    # 64-window tile holds up to ~4000 outputs, more than the two prefetched
+    # chunk slots of the fixed-store kernel cover (2033); the library then
+    # uses the kernel with the general store loop.  Short-code and ordinary
+    # units must both come back bit-exact.
+    rng = np.random.default_rng(77)
+    n = 300_000
+    b = np.full(n, 0x38 if fmt == "fp8_e4m3" else 0x3C, dtype=np.uint8)
+    b ^= rng.integers(0, 2, n, dtype=np.uint8) << 7  # random signs
+    b[rng.integers(0, n, 300)] = rng.integers(0, 256, 300, dtype=np.uint8)
+    u = Unit([b], fmt)
+    assert u.hs.max_tile_symbols > 2033
+    check_identity(u, "long tiles")
+    z = sw.fp8_from_f32(rng.standard_normal(n).astype(np.float32) * 100.0, fmt.split("_")[1])
+    v = Unit([z], fmt)
+    assert v.hs.max_tile_symbols <= 2033
+    check_identity(v, "ordinary tiles")
 
 
 def test_fp8_requires_64_window_tiles_and_8_bit_outputs(unit_tensors):
