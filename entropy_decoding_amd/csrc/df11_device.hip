@@ -19,7 +19,8 @@
 //   dispatch order keeps the addresses in flight compact.  Occupancy
 //   matters: on the 70B block, 6, 5 and 4 workgroups per CU measured 5%,
 //   14% and 33% slower than 7; the LDS budget (fast tables, hierarchical
-//   tables 1.., staging) stays near 20 KiB so that 7-8 fit.  A tile is
+//   tables 1.., staging) stays at 20 KiB so that 8 fit (8 were 2.5-3%
+//   faster than 7).  A tile is
 //   256*C windows of 8 bytes; thread t decodes windows C*t .. C*t + C - 1 as
 //   C independent dependency chains, so each LDS lookup latency is shared by C
 //   codes in flight.
@@ -31,7 +32,8 @@
 // * Phase 1 counts the codes that start in each window, several per step: a
 //   12-bit index into the count table gives the start offsets of every code
 //   wholly inside those 12 bits as a bit mask, so a step adds the popcount of
-//   the mask cut at the window's end.
+//   the mask; the starts a chain's last step finds past the window's end are
+//   taken off once, after the loop.
 // * A wave64 inclusive scan in DPP row shifts and row broadcasts, then an LDS
 //   pass over the 4 wave totals, turns counts into offsets; the tile total
 //   must equal block_out_pos[t+1] - block_out_pos[t].
@@ -39,10 +41,11 @@
 //   multi-symbol table (up to 3 exponents per step) and writes exponent bytes
 //   into an LDS staging buffer at their offsets.  A step writes all 3 slots,
 //   so a window's last step may spill up to 2 bytes onto the next window's
-//   first two outputs; every window rewrites those after a barrier.
-// * The decode loops run until no lane of the wave has work (ballot); lanes
-//   whose chain has finished are masked off for the update, so they neither
-//   count, write nor move.
+//   first two outputs; every window keeps its own first two exponents and
+//   rewrites them after a barrier.
+// * The decode loops are divergent loops: a lane whose chain has finished
+//   leaves the loop (masked off), so it neither counts, writes nor moves,
+//   and the wave runs until no lane has work.
 // * The outputs are assembled 8 at a time from 8 sm bytes and 8 exponent
 //   bytes with byte permutes; the lanes of a wave store 1 KiB contiguously.
 // Codes longer than the fast tables' index walk the hierarchical 8-bit

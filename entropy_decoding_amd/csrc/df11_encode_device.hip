@@ -261,38 +261,46 @@ __global__ __launch_bounds__(kThreads) void enc_emit(EmitArgs a) {
     for (uint32_t i = t; i < nw + 1; i += kThreads) buf[i] = 0;
     __syncthreads();
 
-    // the previous weight's code length, for "first start in a window / tile"
-    uint32_t prev_len = 0;
+    // The previous weight's code length decides whether a code is the first
+    // to start in its window or tile: with a window (or tile) of W >= 32 bits,
+    // the previous code started in an earlier one exactly when the start bit
+    // modulo W is below that length.  The unit's first weight has no
+    // predecessor; a length of 64 makes both tests true for it.  Positions are
+    // kept relative to the workgroup (32 bits); the tests need only the low
+    // bits of the absolute position.
+    uint32_t prev_len = i0 == 0 ? 64u : 0u;
     if (i0 > 0 && i0 <= a.n) {
         using T = typename Fields<FMT>::T;
         prev_len = len_s[Fields<FMT>::sym(static_cast<const T *>(a.w)[i0 - 1])];
     }
-    uint64_t pos = g0 + before;  // start bit of this thread's first code
+    const uint32_t g0lo = uint32_t(g0), wmask = (1u << a.wshift) - 1, tmask = (1u << a.tshift) - 1;
+    uint32_t r = before + (g0lo & 31u);  // start bit of the thread's next code, from base
+    uint32_t last = r;                    // start of the thread's last code
 #pragma unroll
     for (uint32_t k = 0; k < 16; k++) {
         if (k < valid) {
             const uint32_t s = Fields<FMT>::sym(x[k]);
             const uint32_t l = len_s[s], c = code_s[s];
-            const uint64_t prev = pos - prev_len;  // start of the previous code (i > 0)
-            const bool first = i0 + k == 0;
-            if (first || (prev >> a.wshift) < (pos >> a.wshift))
-                a.gaps[pos >> a.wshift] = uint8_t(pos & ((1u << a.wshift) - 1));
-            if (first) a.bop[0] = 0;
-            else if ((prev >> a.tshift) < (pos >> a.tshift)) a.bop[pos >> a.tshift] = uint32_t(i0 + k);
-            const uint64_t r = pos - base;
-            const uint32_t wi = uint32_t(r >> 5), o = uint32_t(r & 31);
-            if (o + l <= 32) {
-                atomicOr(&buf[wi], c << (32 - o - l));
-            } else {
-                atomicOr(&buf[wi], c >> (o + l - 32));
-                atomicOr(&buf[wi + 1], c << (64 - o - l));
+            const uint32_t pl = (g0lo & ~31u) + r;  // low 32 bits of the absolute start bit
+            if ((pl & wmask) < prev_len) {  // first code start in its window
+                const uint64_t pos = base + r;
+                a.gaps[pos >> a.wshift] = uint8_t(pos & wmask);
             }
-            if (i0 + k + 1 == a.n) {  // the last weight: tile boundaries after its start
-                for (uint64_t b = (pos >> a.tshift) + 1; b <= a.n_tiles; b++) a.bop[b] = uint32_t(a.n);
+            if ((pl & tmask) < prev_len) {  // first code start in its tile
+                const uint64_t pos = base + r;
+                a.bop[pos >> a.tshift] = uint32_t(i0 + k);
             }
+            // the code, left-aligned at bit r % 32 of word r / 32, over two words
+            const uint64_t v = uint64_t(c) << (64u - (r & 31u) - l);
+            atomicOr(&buf[r >> 5], uint32_t(v >> 32));
+            atomicOr(&buf[(r >> 5) + 1], uint32_t(v));
+            last = r;
             prev_len = l;
-            pos += l;
+            r += l;
         }
+    }
+    if (valid && i0 + valid == a.n) {  // the last weight: tile boundaries after its start
+        for (uint64_t b = ((base + last) >> a.tshift) + 1; b <= a.n_tiles; b++) a.bop[b] = uint32_t(a.n);
     }
     // sign and mantissa fields (zero past n, like the host encoder's padding);
     // sm_bytes is a multiple of 64, so a thread's 16 or 8 bytes are all inside or all outside
