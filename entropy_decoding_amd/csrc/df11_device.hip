@@ -505,10 +505,6 @@ template <>
 struct OutFmt<DF11_FORMAT_BF16> {
     static constexpr uint32_t kChunk = 8;
     static __device__ __forceinline__ uint32_t rest_off(uint32_t g) { return g; }
-    static __device__ __forceinline__ void store(const KArgs &a, uint32_t gi, uint2 s8,
-                                                 const uint8_t *ex) {
-        store8(a, gi, s8, ex);
-    }
     static constexpr uint32_t kElemBytes = 2;
     static __device__ __forceinline__ uint4 chunk(uint2 s8, const uint8_t *ex) {
         const uint2 e8 = *reinterpret_cast<const uint2 *>(ex);
@@ -560,10 +556,6 @@ struct OutFp8 {
         v.z = assemble(spread(s8.y, 0x01010000u), e16.z);
         v.w = assemble(spread(s8.y, 0x03030202u), e16.w);
         return v;
-    }
-    static __device__ __forceinline__ void store(const KArgs &a, uint32_t gi, uint2 s8,
-                                                 const uint8_t *ex) {
-        *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.out) + (gi - a.out_shift)) = chunk(s8, ex);
     }
     static __device__ __forceinline__ void store_at(const KArgs &a, int64_t base, uint32_t c,
                                                     uint2 s8, const uint8_t *ex) {
@@ -645,7 +637,9 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi, uint32_t fi
     }
     __syncthreads();
     // Let the first tile's loads complete here, so that the wait at the top
-    // of the tile loop is set by the loop's own paths (vmcnt(0) on gfx9).
+    // of the tile loop is set by the loop's own paths.  The immediate is the
+    // gfx9 s_waitcnt encoding of vmcnt(0) with expcnt and lgkmcnt left at
+    // their maxima (7 in bits 6:4, 15 in bits 11:8).
     if constexpr (Epi::kAlways) __builtin_amdgcn_s_waitcnt(0x0F70);
     const uint16_t *lut = reinterpret_cast<const uint16_t *>(dyn);
     uint8_t *ebuf = dyn + a.ebuf_off + wid * a.exp_cap;
