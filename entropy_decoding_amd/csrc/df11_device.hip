@@ -617,8 +617,10 @@ __device__ __forceinline__ uint2 chunk_sm(const KArgs &a, const uint2 (&smv)[JP]
 // fused GEMV and GEMM consume them (df11_decompress_gemv, _gemm).  Epi::kSmv
 // says whether the tile's sign+mantissa bytes are loaded in lane order
 // (chunk lane + 64 j in smv[j]) before the decode; Epi::prefetch may load
-// whatever else the epilogue needs at that point.  The wave takes tiles
-// first + slot, first + slot + n_slots, ... below first + count.
+// whatever else the epilogue needs at that point; Epi::kAlways says that the
+// epilogue also runs on a rejected tile (with an empty range), so that every
+// path through the loop issues its memory instructions.  The wave takes
+// tiles first + slot, first + slot + n_slots, ... below first + count.
 template <int JP, int FMT, class Epi>
 __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi, uint32_t first,
                                            uint32_t count, uint32_t slot, uint32_t n_slots) {
@@ -696,16 +698,16 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi, uint32_t fi
         }
 
         if (ok) {
-            uint32_t first[1], dst[1];
-            first[0] = lds_addr(ebuf) + (P0 - A0) + incl - cnt[0];
-            dst[0] = first[0];
+            uint32_t beg[1], dst[1];  // LDS addresses of the window's first output
+            beg[0] = lds_addr(ebuf) + (P0 - A0) + incl - cnt[0];
+            dst[0] = beg[0];
             uint32_t f01[1];
             decode_codes<1>(win, gap, lim, fast, lut, a.lut_last, dst, f01);
             // keep the compiler from moving LDS accesses across the steps below;
             // the hardware keeps one wave's LDS operations in order
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             {
-                lds8 *o = (lds8 *)size_t(first[0]);
+                lds8 *o = (lds8 *)size_t(beg[0]);
                 if (cnt[0]) o[0] = uint8_t(f01[0]);
                 if (cnt[0] > 1) o[1] = uint8_t(f01[0] >> 8);
             }
