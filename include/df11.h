@@ -309,7 +309,8 @@ int df11_histogram_device(uint32_t format, const void *w, uint64_t n, uint64_t *
                           df11_hip_stream st);
 
 /* Device scratch df11_encode_device needs for n weights (per-4096-weight bit
- * totals and start bits). */
+ * totals, start bits, and the two boundary-word shares of each 4096-weight
+ * group). */
 uint64_t df11_encode_device_scratch_bytes(uint64_t n_weights);
 
 /* Device buffers of df11_encode_device (all device memory, 16-byte aligned;
