@@ -1146,6 +1146,14 @@ struct GemmDesc {
     uint32_t x_off[DF11_GEMV_MAX_TENSORS], y_off[DF11_GEMV_MAX_TENSORS];
     // reordered activations: 16-byte chunks ch0[k] .. ch0[k+1]-1 of the workspace
     uint32_t ch0[DF11_GEMV_MAX_TENSORS + 1];  // n .. 16: the total
+    // K segments: a row block of matrix k is split into seg[k] runs of
+    // sbl[k] 32-column sub-blocks (the last may be shorter), one workgroup
+    // each, segment-major; with seg[k] > 1 the partial sums go to the
+    // workspace at p_off[k] (float index, seg[k] slices of rows x tokens)
+    uint32_t seg[DF11_GEMV_MAX_TENSORS], sbl[DF11_GEMV_MAX_TENSORS];
+    uint32_t p_off[DF11_GEMV_MAX_TENSORS];
+    // float4s of the split matrices' outputs: q0[k] .. q0[k+1]-1; n .. 16: the total
+    uint32_t q0[DF11_GEMV_MAX_TENSORS + 1];
 };
 
 // The activations in the B operand's order: chunk j of matrix k's slice is
@@ -1247,22 +1255,26 @@ struct GemmEpi {
     }
 };
 
-// One workgroup per 16-row block (blocks of the widest matrices first, in the
-// XCD-grouped order).  The block's tiles are found in block_out_pos; each
-// wave takes every fourth.
+// One workgroup per 16-row block and K segment (longest segments first, in
+// the XCD-grouped order).  The segment's tiles are found in block_out_pos;
+// each wave takes every fourth.  Matrices far wider than the narrowest had
+// whole row blocks take up to 3.5 times as long as the rest (the 70B
+// down projection), which left a tail of few, long workgroups.
 template <int NB>
 __global__ __launch_bounds__(kThreads) void df11_decode_gemm(KArgs a, GemmDesc g, const uint16_t *xs,
-                                                             float *y) {
+                                                             float *y, float *part) {
     const uint32_t mb = xcd_grouped(blockIdx.x);
     if (mb >= g.mb0[DF11_GEMV_MAX_TENSORS]) return;  // uniform: the grid is rounded up
     uint32_t k = 0;
 #pragma unroll
     for (uint32_t m = 1; m <= DF11_GEMV_MAX_TENSORS; m++) k += uint32_t(mb >= g.mb0[m]);
-    const uint32_t cols = g.cols[k], rb = mb - g.mb0[k];
+    const uint32_t cols = g.cols[k], rows = g.rows[k], w = mb - g.mb0[k];
+    const uint32_t sg = w / (rows / 16), rb = w - sg * (rows / 16);
+    const uint32_t sbS = sg * g.sbl[k], sbE = min(sbS + g.sbl[k], cols / 32);
     GemmEpi<NB> epi;
-    epi.e0 = g.off[k] + rb * 16 * cols;
-    epi.e1 = epi.e0 + 16 * cols;
-    epi.xk = xs + 8 * uint64_t(g.ch0[k]);
+    epi.e0 = g.off[k] + rb * 16 * cols + 512 * sbS;
+    epi.e1 = g.off[k] + rb * 16 * cols + 512 * sbE;
+    epi.xk = xs + 8 * (uint64_t(g.ch0[k]) + uint64_t(sbS) * 64 * NB);
     epi.cols = cols;
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) epi.acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1290,8 +1302,9 @@ __global__ __launch_bounds__(kThreads) void df11_decode_gemm(KArgs a, GemmDesc g
     }
     __syncthreads();
     if (wid == 0) {
-        const uint32_t rows = g.rows[k];
-        float *yk = y + g.y_off[k] + 16 * rb + 4 * (lane >> 4);
+        float *yk = (g.seg[k] > 1 ? part + g.p_off[k] + uint64_t(sg) * 16 * NB * rows
+                                  : y + g.y_off[k]) +
+                    16 * rb + 4 * (lane >> 4);
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
             f32x4 v = epi.acc[nb];
@@ -1301,6 +1314,26 @@ __global__ __launch_bounds__(kThreads) void df11_decode_gemm(KArgs a, GemmDesc g
             *reinterpret_cast<f32x4 *>(yk + uint64_t(16 * nb + (lane & 15u)) * rows) = v;
         }
     }
+}
+
+// y of the split matrices: the sum of their K segments' partial sums, in
+// segment order.  One thread per float4.
+__global__ __launch_bounds__(kThreads) void df11_gemm_reduce(GemmDesc g, uint32_t n_tok,
+                                                             const float *part, float *y) {
+    const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
+    if (j >= g.q0[DF11_GEMV_MAX_TENSORS]) return;
+    uint32_t k = 0;
+#pragma unroll
+    for (uint32_t m = 1; m <= DF11_GEMV_MAX_TENSORS; m++) k += uint32_t(j >= g.q0[m]);
+    const uint32_t r = 4 * (j - g.q0[k]);
+    const uint64_t slice = uint64_t(n_tok) * g.rows[k];
+    const float *p = part + g.p_off[k] + r;
+    float4 v = *reinterpret_cast<const float4 *>(p);
+    for (uint32_t s = 1; s < g.seg[k]; s++) {
+        const float4 u = *reinterpret_cast<const float4 *>(p + s * slice);
+        v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    *reinterpret_cast<float4 *>(y + g.y_off[k] + r) = v;
 }
 
 template <int NB>
@@ -1525,11 +1558,32 @@ int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t,
                : DF11_E_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+// K segments of matrix k's row blocks: row blocks of matrices much wider
+// than the narrowest (at least 4096 columns) are split so that every
+// workgroup decodes about as many weights
+uint32_t gemm_segments(const df11_gemv_tensor *t, uint32_t n_tensors, uint32_t k) {
+    uint32_t ref = ~0u;
+    for (uint32_t i = 0; i < n_tensors; i++) ref = std::min(ref, t[i].cols);
+    ref = std::max(ref, 4096u);
+    return std::max(1u, (t[k].cols + ref - 1) / ref);
+}
+}  // namespace
+
+extern "C" {
+
 uint64_t df11_decompress_gemm_scratch_bytes(const df11_gemv_tensor *t, uint32_t n_tensors,
                                             uint32_t n_tokens) {
     if (!t && n_tensors) return 0;
     uint64_t b = 0;
     for (uint32_t k = 0; k < n_tensors; k++) b += 2ull * n_tokens * t[k].cols;
+    b = (b + 15) / 16 * 16;
+    for (uint32_t k = 0; k < n_tensors; k++) {
+        const uint32_t sg = gemm_segments(t, n_tensors, k);
+        if (sg > 1) b += 4ull * sg * n_tokens * t[k].rows;
+    }
     return b;
 }
 
@@ -1545,14 +1599,19 @@ int df11_decompress_gemm(const df11_device_stream *s, const df11_gemv_tensor *t,
         !x || !y || !scratch || !aligned(x, 16) || !aligned(y, 16) || !aligned(scratch, 16) ||
         scratch_bytes < df11_decompress_gemm_scratch_bytes(t, n_tensors, n_tokens))
         return DF11_E_INVALID;
-    // widest matrices first: their row blocks take the longest
-    uint32_t order[DF11_GEMV_MAX_TENSORS];
-    for (uint32_t k = 0; k < n_tensors; k++) order[k] = k;
+    // longest segments first: their workgroups take the longest
+    uint32_t order[DF11_GEMV_MAX_TENSORS], sbl[DF11_GEMV_MAX_TENSORS], seg[DF11_GEMV_MAX_TENSORS];
+    for (uint32_t k = 0; k < n_tensors; k++) {
+        order[k] = k;
+        seg[k] = gemm_segments(t, n_tensors, k);
+        sbl[k] = (t[k].cols / 32 + seg[k] - 1) / seg[k];
+        seg[k] = (t[k].cols / 32 + sbl[k] - 1) / sbl[k];  // no empty segment
+    }
     std::stable_sort(order, order + n_tensors,
-                     [t](uint32_t i, uint32_t j) { return t[i].cols > t[j].cols; });
+                     [&sbl](uint32_t i, uint32_t j) { return sbl[i] > sbl[j]; });
     GemmDesc g{};
     g.n = n_tensors;
-    uint64_t off = 0, mbs = 0, chunks = 0;
+    uint64_t off = 0, mbs = 0, chunks = 0, pw = 0, q4 = 0;
     for (uint32_t k = 0; k < n_tensors; k++) {
         // in the unit the matrices follow one another in the caller's order
         if (t[k].w_offset != off || t[k].rows == 0 || t[k].rows % 16 || t[k].cols == 0 ||
@@ -1572,13 +1631,23 @@ int df11_decompress_gemm(const df11_device_stream *s, const df11_gemv_tensor *t,
         g.x_off[i] = uint32_t(d.x_offset);
         g.y_off[i] = uint32_t(d.y_offset);
         g.ch0[i] = uint32_t(chunks);
-        mbs += d.rows / 16;
+        g.seg[i] = seg[order[i]];
+        g.sbl[i] = sbl[order[i]];
+        g.p_off[i] = uint32_t(pw);
+        g.q0[i] = uint32_t(q4);
+        mbs += uint64_t(d.rows / 16) * g.seg[i];
         chunks += uint64_t(n_tokens) * d.cols / 8;
+        if (g.seg[i] > 1) {
+            pw += uint64_t(g.seg[i]) * n_tokens * d.rows;
+            q4 += uint64_t(n_tokens) * d.rows / 4;
+        }
     }
-    if (chunks >= (uint64_t(1) << 32)) return DF11_E_INVALID;
+    if (chunks >= (uint64_t(1) << 32) || pw >= (uint64_t(1) << 32) || mbs >= (uint64_t(1) << 31))
+        return DF11_E_INVALID;
     for (uint32_t k = n_tensors; k <= DF11_GEMV_MAX_TENSORS; k++) {
         g.mb0[k] = uint32_t(mbs);
         g.ch0[k] = uint32_t(chunks);
+        g.q0[k] = uint32_t(q4);
     }
     a.status = d_status;
     a.out_lo = 0;
@@ -1598,10 +1667,16 @@ int df11_decompress_gemm(const df11_device_stream *s, const df11_gemv_tensor *t,
         return DF11_E_HIP;
     const uint32_t grid = uint32_t((mbs + kXcdBlock - 1) / kXcdBlock * kXcdBlock);
     const uint16_t *xsp = xs;
-    void *args[] = {&a, &g, &xsp, &y};
-    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, lds, hs) == hipSuccess
-               ? DF11_OK
-               : DF11_E_HIP;
+    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(scratch) +
+                                            (2 * chunks * 8 + 15) / 16 * 16);
+    void *args[] = {&a, &g, &xsp, &y, &part};
+    if (hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, lds, hs) != hipSuccess)
+        return DF11_E_HIP;
+    if (q4 && df11_detail::launch(df11_gemm_reduce, dim3(uint32_t((q4 + kThreads - 1) / kThreads)),
+                                  dim3(kThreads), 0, hs, g, n_tokens,
+                                  static_cast<const float *>(part), y) != hipSuccess)
+        return DF11_E_HIP;
+    return DF11_OK;
 }
 
 }  // extern "C"

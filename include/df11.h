@@ -457,12 +457,17 @@ int df11_gemm_order(const uint16_t *w, uint32_t rows, uint32_t cols, uint16_t *o
  * aligned and not overlapping, x_offset_k multiples of 8, y_offset_k of 4.  scratch: at least
  * df11_decompress_gemm_scratch_bytes(tensors, n_tensors, n_tokens) bytes
  * (each matrix's activations reordered for the matrix cores, 2 * n_tokens *
- * cols_k bytes); no initialisation needed.  Products are exact; sums are
- * float32 in the matrix cores, per 16-row block each of four waves adding
- * its 32-column sub-blocks in order, then the four waves in order
- * (deterministic).  Weights outside a decoded tile enter as zeros, so x must
- * be finite.  Two launches on st, no allocation; calls sharing a scratch
- * buffer must not overlap.  Corrupt tiles are reported in *d_status as by
+ * cols_k bytes, then float32 partial sums of the split matrices); no
+ * initialisation needed.  Products are exact; sums are float32 in the
+ * matrix cores, per 16-row block and K segment each of four waves adding its
+ * 32-column sub-blocks in order, then the four waves in order, then the
+ * segments in order (deterministic).  A matrix with cols_k above
+ * R = max(4096, min_j cols_j) has its row blocks split into at
+ * most ceil(cols_k / R) K segments of whole sub-blocks, so that every
+ * workgroup decodes about as many weights.  Weights
+ * outside a decoded tile enter as zeros, so x must be finite.  Two launches
+ * on st (three when a matrix is split), no allocation; calls sharing a
+ * scratch buffer must not overlap.  Corrupt tiles are reported in *d_status as by
  * df11_decompress_block (the rows they hold get wrong values).
  * DF11_E_INVALID for other shapes, formats or layouts.
  */

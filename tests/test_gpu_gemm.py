@@ -7,7 +7,8 @@ equal the oracle's float64 product bit for bit; this pins the sub-block
 order, the lane mapping, the masking of shared chunks and the cross-wave sum.
 On Gaussian data the results must lie within a rounding bound that assumes
 nothing about the matrix cores' internal order: at most one rounding of at
-most 2u per addition, K + K/32 + 3 additions per output.
+most 2u per addition, K + K/32 + 3 additions per output, plus one per extra
+K segment of a split matrix (at most ceil(K / 4096) segments).
 """
 
 import numpy as np
@@ -100,7 +101,7 @@ def _bound(tensors, shapes, x, n):
     xa = np.abs(oracle.bf16_to_f64(x))
     out, wo, xo = [], 0, 0
     for r, c in shapes:
-        d = c + c // 32 + 3
+        d = c + c // 32 + 3 + (c + 4095) // 4096 - 1
         g = 2 * d * U / (1 - 2 * d * U)
         W = w[wo:wo + r * c].reshape(r, c)
         X = xa[xo:xo + n * c].reshape(n, c)
@@ -124,6 +125,31 @@ def test_gemm_gaussian_data_within_the_bound_and_deterministic():
     ref = oracle.gemm(np.concatenate(tensors), shapes, x, n)
     err = np.abs(y1 - ref)
     assert np.all(err <= _bound(tensors, shapes, x, n) + 1e-30)
+
+
+@pytest.mark.parametrize("n", [16, 64])
+def test_gemm_split_rows_integer_exact_and_gaussian_bound(n):
+    """Matrices 3.25 and 2.02 times wider than the narrowest (4096 columns)
+    are split into K segments of 104 and 87/87/85 sub-blocks: integer data
+    stays exact, Gaussian data within the bound, and repeated calls agree."""
+    rng = np.random.default_rng(300 + n)
+    shapes = [(32, 4096), (16, 13312), (48, 8288)]
+    u = _int_unit(rng, shapes)
+    x = _bf16(rng.integers(-3, 4, sum(n * c for _, c in shapes)).astype(np.float32))
+    y, st = u.run(x, n, "split integers")
+    assert st == 0
+    ref = oracle.gemm(np.concatenate(u.tensors), shapes, x, n)
+    assert np.array_equal(y, ref), np.flatnonzero(y != ref)[:10]
+
+    tensors = [_bf16(rng.standard_normal(r * c) * 0.02) for r, c in shapes]
+    g = GemmUnit(tensors, shapes)
+    x = _bf16(rng.standard_normal(sum(n * c for _, c in shapes)))
+    y1, st1 = g.run(x, n, "split gaussian")
+    y2, st2 = g.run(x, n, "split gaussian again")
+    assert st1 == st2 == 0
+    assert np.array_equal(y1, y2)
+    ref = oracle.gemm(np.concatenate(tensors), shapes, x, n)
+    assert np.all(np.abs(y1 - ref) <= _bound(tensors, shapes, x, n))
 
 
 def test_gemm_8b_block_sampled():
@@ -187,15 +213,18 @@ def test_gemm_argument_errors_and_corruption():
         assert int(st.item()) == ed.DF11_E_CORRUPT
 
 
-def test_gemm_scratch_needs_no_initialisation_and_is_checked():
+@pytest.mark.parametrize("shapes,split", [([(32, 512), (16, 256)], 0),
+                                          ([(16, 4096), (16, 8224)], 3)])
+def test_gemm_scratch_needs_no_initialisation_and_is_checked(shapes, split):
+    """Neither the reordered activations nor the K segments' partial sums
+    (8224 columns against 4096: three segments) need clearing."""
     rng = np.random.default_rng(11)
-    shapes = [(32, 512), (16, 256)]
     u = _int_unit(rng, shapes)
     n = 32
     layout = ed.gemm_layout(shapes, n)
     x = torch.from_numpy(_bf16(rng.integers(-3, 4, layout[2]).astype(np.float32)).view(np.int16)).cuda()
     need = ed.df11_decompress_gemm_scratch_bytes(layout, n)
-    assert need == 2 * n * (512 + 256)
+    assert need == 2 * n * sum(c for _, c in shapes) + 4 * split * n * shapes[-1][0]
     ys = []
     for fill in (0x00, 0xFF):
         scr = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
@@ -204,6 +233,8 @@ def test_gemm_scratch_needs_no_initialisation_and_is_checked():
         torch.cuda.synchronize()
         ys.append(y)
     assert torch.equal(ys[0], ys[1])
+    ref = oracle.gemm(np.concatenate(u.tensors), shapes, x.cpu().numpy().view(np.uint16), n)
+    assert np.array_equal(ys[0].cpu().numpy().astype(np.float64), ref)
     with pytest.raises(ed.Df11Error):
         ed.df11_decompress_gemm(u.ds, layout, n, x, ys[0],
                                 torch.zeros(need - 16, dtype=torch.uint8, device="cuda"))

@@ -330,6 +330,16 @@ def test_fused_workspace_sizes():
     lay = ed.gemm_layout(shapes, 48)
     assert ed.df11_decompress_gemm_scratch_bytes(lay, 48) == 2 * 48 * (1024 + 4096)
     assert ed.LIB.df11_decompress_gemm_scratch_bytes(None, 0, 16) == 0
+    # 12288 and 8224 columns against the narrowest 4096: three K segments
+    # each, whose float32 partial sums follow the activations
+    lay = ed.gemm_layout([(16, 4096), (32, 12288), (48, 8224)], 16)
+    assert ed.df11_decompress_gemm_scratch_bytes(lay, 16) == (
+        2 * 16 * (4096 + 12288 + 8224) + 4 * 3 * 16 * (32 + 48))
+    # the narrowest counts as 4096 at least: 1024 is not split, 8192 has two
+    # segments, 12288 three
+    lay = ed.gemm_layout([(16, 1024), (16, 8192), (16, 12288)], 32)
+    assert ed.df11_decompress_gemm_scratch_bytes(lay, 32) == (
+        2 * 32 * (1024 + 8192 + 12288) + 4 * (2 + 3) * 32 * 16)
     rng = np.random.default_rng(3)
     w = (rng.standard_normal(64 * 1024).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     cb = ed.df11_build_codebook([w])
