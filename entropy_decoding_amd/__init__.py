@@ -170,6 +170,8 @@ def _load():
                                         ctypes.c_void_p, ctypes.c_void_p]
     L.df11_decompress_tensor.argtypes = [ctypes.POINTER(df11_device_stream), ctypes.c_uint32,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.df11_window_counts.argtypes = [ctypes.POINTER(df11_device_stream), ctypes.c_void_p,
+                                     ctypes.c_void_p]
     L.df11_status_string.argtypes = [ctypes.c_int]
     L.df11_status_string.restype = ctypes.c_char_p
     vp = ctypes.c_void_p
@@ -209,7 +211,8 @@ def _load():
               L.df11_pipeline_destroy, L.df11_pipeline_decompress, L.df11_pipeline_acquire,
               L.df11_pipeline_release, L.df11_gemv_bf16, L.df11_build_codebook_from_counts,
               L.df11_encode_size_from_counts, L.df11_histogram_device, L.df11_encode_device,
-              L.df11_decompress_gemv, L.df11_gemm_order, L.df11_decompress_gemm):
+              L.df11_decompress_gemv, L.df11_gemm_order, L.df11_decompress_gemm,
+              L.df11_window_counts):
         f.restype = ctypes.c_int
     return L
 
@@ -444,6 +447,18 @@ def df11_decompress_tensor(ds: DeviceStream, k: int, out, status=None, stream=No
            LIB.df11_decompress_tensor(ctypes.byref(ds.desc), int(k),
                                       ctypes.c_void_p(out.data_ptr()), sp,
                                       _stream_handle(stream)))
+
+
+def df11_window_counts(ds: DeviceStream, counts, stream=None) -> None:
+    """Phase 1 of the decode on its own: ``counts`` (a device int32 tensor of
+    n_tiles * tile_windows elements) receives each stream window's number of
+    code starts."""
+    n = int(ds.desc.n_tiles) * int(ds.desc.tile_windows)
+    if counts.numel() != n or counts.element_size() != 4 or not counts.is_contiguous():
+        raise Df11Error(f"df11_window_counts: counts must be {n} contiguous 4-byte elements")
+    _check("df11_window_counts",
+           LIB.df11_window_counts(ctypes.byref(ds.desc), ctypes.c_void_p(counts.data_ptr()),
+                                  _stream_handle(stream)))
 
 
 # ---------------------------------------------------------------- block pipeline

@@ -835,6 +835,37 @@ __global__ __launch_bounds__(kThreads) void df11_decode_wave_fixed(KArgs a) {
     wave_tiles<JP, FMT>(a, epi);
 }
 
+// ------------------------------------------------------------ phase-1 counts
+// counts[j] = the codes whose first bit lies in stream window j, from the
+// decode kernels' own first phase (count_codes), one window per thread: a
+// diagnostic that checks that phase window by window.
+__global__ __launch_bounds__(kThreads) void df11_count_windows(KArgs a, uint32_t n_windows,
+                                                               uint32_t *counts) {
+    __shared__ __align__(16) uint8_t fast[kLutOff];
+    extern __shared__ __align__(16) uint8_t dyn[];
+    const uint32_t t = threadIdx.x;
+    for (uint32_t i = 16 * t; i < a.lds_tables; i += 16 * kThreads) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(a.tables + (i < kLutOff ? i : i + 512));
+        *reinterpret_cast<uint4 *>(i < kLutOff ? fast + i : dyn + (i - kLutOff)) = v;
+    }
+    __syncthreads();
+    const uint16_t *lut = reinterpret_cast<const uint16_t *>(dyn);
+    const uint32_t j = blockIdx.x * kThreads + t;
+    if (j >= n_windows) return;
+    // the window's 8 bytes and the 4 after it (the stream ends in 4 padding bytes)
+    const uint32_t *wp = reinterpret_cast<const uint32_t *>(a.stream + 8 * uint64_t(j));
+    uint32_t d[3];
+#pragma unroll
+    for (int k = 0; k < 3; k++) d[k] = __builtin_bswap32(wp[k]);
+    Windows<1> win;
+    win.init(d);
+    const uint64_t base = 64 * uint64_t(j);
+    uint32_t gap[1] = {a.gaps[j]}, cnt[1];
+    uint32_t lim[1] = {a.total_bits > base ? uint32_t(min<uint64_t>(64, a.total_bits - base)) : 0u};
+    count_codes<1>(win, gap, lim, fast, lut, a.lut_last, cnt);
+    counts[j] = cnt[0];
+}
+
 // ---------------------------------------------------------------- fused GEMV
 //
 // y = W x for the matrices of a BF16 unit, straight from the compressed
@@ -1457,6 +1488,26 @@ int df11_decompress_block(const df11_device_stream *s, void *out, int32_t *d_sta
     a.out_hi = uint32_t(s->n_weights);
     a.out_shift = 0;
     return launch(s, a, uint32_t(s->n_tiles), static_cast<hipStream_t>(st));
+}
+
+int df11_window_counts(const df11_device_stream *s, uint32_t *counts, df11_hip_stream st) {
+    KArgs a{};
+    int rc = prepare(s, a);
+    if (rc != DF11_OK) return rc;
+    const uint64_t n = uint64_t(s->n_tiles) * s->tile_windows;
+    if (n == 0) return DF11_OK;
+    if (!counts || !aligned(counts, 4) || n >= (uint64_t(1) << 32)) return DF11_E_INVALID;
+    const void *fn = reinterpret_cast<const void *>(&df11_count_windows);
+    const size_t lds = 512u * size_t(a.lut_last);
+    if (lds > 65536 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+        return DF11_E_INVALID;
+    const uint32_t nw = uint32_t(n);
+    void *args[] = {&a, const_cast<uint32_t *>(&nw), &counts};
+    return hipLaunchKernel(fn, dim3(uint32_t((n + kThreads - 1) / kThreads)), dim3(kThreads), args,
+                           lds, static_cast<hipStream_t>(st)) == hipSuccess
+               ? DF11_OK
+               : DF11_E_HIP;
 }
 
 int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, void *out,

@@ -288,6 +288,20 @@ int df11_decompress_block(const df11_device_stream *s, void *out, int32_t *d_sta
 int df11_decompress_tensor(const df11_device_stream *s, uint32_t k, void *out,
                            int32_t *d_status, df11_hip_stream st);
 
+/*
+ * df11_window_counts -- device, diagnostic.  The first phase of the
+ * two-phase decode (DFloat11 abstract: each thread counts the codes of its
+ * own window before the outputs are placed) run on its own, one window per
+ * thread, with the same device code the decompress kernels use:
+ * counts[j] = the number of codes whose first bit lies in stream bits
+ * [64 j, 64 j + 64), for every window j < n_tiles * tile_windows.  counts:
+ * device, caller-owned, 4-byte aligned, n_tiles * tile_windows uint32
+ * entries.  The prefix sums at tile boundaries are block_out_pos; a window
+ * whose bits are no valid code gets 2^20 added.  One launch on st,
+ * asynchronous.  DF11_E_INVALID for a bad descriptor or a null counts.
+ */
+int df11_window_counts(const df11_device_stream *s, uint32_t *counts, df11_hip_stream st);
+
 /* Static description of a status code. */
 const char *df11_status_string(int status);
 

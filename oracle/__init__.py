@@ -211,6 +211,17 @@ def aux(tensors, cb: Codebook, tile_windows: int, window_bytes: int, fast: bool 
     return gaps, bop
 
 
+def window_counts(sym: np.ndarray, lens, n_windows: int, window_bytes: int = 8) -> np.ndarray:
+    """count_j = number of codes whose first bit lies in window j (bits
+    [8 B j, 8 B (j+1))), for the symbol sequence sym coded with lengths lens.
+    Code i starts at the sum of the lengths of codes 0 .. i-1 (DFloat11
+    abstract: the first of the two phases counts each thread's codes)."""
+    sym = np.ascontiguousarray(sym).reshape(-1)
+    ln = np.asarray(lens, dtype=np.int64)[sym]
+    starts = np.cumsum(ln) - ln
+    return np.bincount(starts // (8 * window_bytes), minlength=n_windows).astype(np.uint32)
+
+
 def decode(stream: np.ndarray, start_bit: int, end_bit: int, lens, sm: np.ndarray,
            n: int | None = None) -> np.ndarray:
     """Bit-serial decode of n symbols from start_bit; returns uint16 BF16 bit patterns."""

@@ -63,6 +63,23 @@ def check_identity(u, label, poisons=(0xA5, 0x5A)):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_phase1_window_counts(fmt, unit_tensors):
+    """The first decode phase, window by window, against the oracle's count of
+    code starts on the FP8 exponent symbols."""
+    (w,) = unit_tensors("0")
+    b = _fp8(w, fmt)
+    sym, _ = oracle.fp8_split(b, fmt.split("_")[1])
+    lens = oracle.code_lengths(oracle.histogram_symbols(sym))
+    u = Unit([b], fmt)
+    n = int(u.hs.n_tiles) * 64
+    c = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    say(f"[gpu] df11_window_counts {fmt} cfg0 windows={n}")
+    ed.df11_window_counts(u.ds, c)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cpu().numpy().view(np.uint32), oracle.window_counts(sym, lens, n))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_fp8_config0_every_output_equals_the_oracle(fmt, unit_tensors):
     (w,) = unit_tensors("0")
     b = _fp8(w, fmt)

@@ -195,6 +195,51 @@ def test_32_bit_codes_walk_four_table_levels():
     check_sampled_tiles(u, out, 8)
 
 
+# ------------------------------------------------------------------ phase 1 alone
+
+
+def check_window_counts(u, sym, label):
+    """df11_window_counts (the decode's first phase, window by window) against
+    the oracle's count of code starts per window, with the oracle's lengths."""
+    ocb_lens = oracle.code_lengths(oracle.histogram_symbols(sym))
+    lens, _ = ed.codebook_arrays(u.cb)
+    assert np.array_equal(np.asarray(lens), ocb_lens)
+    n = int(u.hs.n_tiles) * u.tw
+    c = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    say(f"[gpu] df11_window_counts {label} windows={n}")
+    ed.df11_window_counts(u.ds, c)
+    torch.cuda.synchronize()
+    ref = oracle.window_counts(sym, ocb_lens, n)
+    got = c.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+
+
+@pytest.mark.parametrize("tw", [64, 256, 512])
+def test_phase1_window_counts_config0(tw, unit_tensors):
+    (w,) = unit_tensors("0")
+    check_window_counts(Unit([w], tw), oracle.exponents(w), f"cfg0 T={tw}")
+
+
+def test_phase1_window_counts_32_bit_codes_and_one_bit_codes():
+    f = [1, 1]
+    while len(f) < 36:
+        f.append(f[-1] + f[-2])
+    sym = np.repeat(np.arange(36, dtype=np.uint16) + 90, f)
+    np.random.default_rng(9).shuffle(sym)
+    w = ((sym << 7) | (np.arange(sym.size) & 0x807F)).astype(np.uint16)
+    u = Unit([w])
+    assert u.cb.max_len == 32
+    check_window_counts(u, oracle.exponents(w), "fibonacci 32-bit codes")
+    w1 = np.full(100003, 0x3F80, dtype=np.uint16)  # one exponent: one-bit codes
+    check_window_counts(Unit([w1]), oracle.exponents(w1), "single exponent")
+
+
+def test_phase1_window_counts_8b_block_full_size():
+    tensors = sw.gen_unit(sw.config("1").units[0])
+    u = Unit(tensors)
+    check_window_counts(u, oracle.exponents(_cat(tensors)), "cfg1 block")
+
+
 # ------------------------------------------------------------------ failure paths
 
 

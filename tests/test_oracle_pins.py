@@ -203,6 +203,42 @@ def test_uniform_256_exponents_stream_is_the_exponent_bytes():
     assert np.array_equal(bop, np.minimum(np.arange(bop.size) * 32, e.size).astype(np.uint32))
 
 
+def test_window_counts_closed_forms():
+    """Every code 8 bits long: eight starts in each full 64-bit window; a
+    hand-worked dyadic code; an empty input."""
+    rng = np.random.default_rng(6)
+    e = np.repeat(np.arange(256, dtype=np.uint8), 3)
+    rng.shuffle(e)
+    c = oracle.window_counts(e, np.full(256, 8), 100)
+    assert np.array_equal(c, np.r_[np.full(96, 8), np.zeros(4)].astype(np.uint32))
+    # lengths 1, 2, 3, 3 (symbols 0..3); 40 codes of symbol 3 then 10 of symbol 0:
+    # 120 bits of 3-bit codes (starts 0, 3, .., 117: 22 in window 0, 18 in
+    # window 1 (starts 66 .. 117)), then 1-bit codes at bits 120 .. 129
+    # (8 in window 1, 2 in window 2)
+    sym = np.r_[np.full(40, 3), np.zeros(10)].astype(np.uint8)
+    lens = np.zeros(256, dtype=np.uint8)
+    lens[:4] = [1, 2, 3, 3]
+    assert oracle.window_counts(sym, lens, 4).tolist() == [22, 26, 2, 0]
+    assert oracle.window_counts(np.zeros(0, np.uint8), lens, 3).tolist() == [0, 0, 0]
+
+
+@pytest.mark.parametrize("tiles,bpt", [(4, 8), (64, 8)])
+def test_window_counts_agree_with_the_aux_arrays(tiles, bpt):
+    """The counts summed per tile are block_out_pos's differences and a window
+    has no code start exactly when its gap is 255 (the aux arrays come from
+    the C oracle's own start-position loop)."""
+    rng = np.random.default_rng(tiles + bpt)
+    w = ((rng.standard_normal(40000).astype(np.float32) * 0.02).view(np.uint32) >> 16).astype(np.uint16)
+    w[::101] = 0x7F80
+    cb = oracle.codebook(w)
+    gaps, bop = oracle.aux(w, cb, tiles, bpt)
+    c = oracle.window_counts(oracle.exponents(w), cb.lens, gaps.size, bpt)
+    assert int(c.sum()) == w.size
+    per_tile = c.reshape(-1, tiles).sum(axis=1, dtype=np.int64)
+    assert np.array_equal(np.r_[0, np.cumsum(per_tile)], bop.astype(np.int64))
+    assert np.array_equal(c == 0, gaps == 255)
+
+
 # ------------------------------------------------------------ round trips
 
 
