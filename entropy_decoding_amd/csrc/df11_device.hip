@@ -1211,8 +1211,11 @@ struct GemmEpi {
     const uint16_t *xk;  // the matrix's reordered activations (chunk j at xk + 8 j)
     uint32_t cols;
     f32x4 acc[NB];
-    uint2 pre[kGemmPre];
-    uint32_t sb0;  // row-block sub-block of pre[0]
+    uint2 pre[kGemmPre];  // sm bytes of the tile's first sub-blocks
+    // B operands loaded before A is built (its work covers part of their
+    // latency) with one 16-token group; after it with more, which keeps
+    // fewer registers live (early: 16 tokens 3% faster, 32 tokens 2% slower)
+    static constexpr bool kEarly = NB == 1;
 
     // the lane's chunk of sub-block sb (relative to the row block)
     __device__ __forceinline__ uint32_t chunk_at(uint32_t sb, uint32_t lane) const {
@@ -1222,13 +1225,64 @@ struct GemmEpi {
     __device__ __forceinline__ void prefetch(const KArgs &a, uint32_t P0, uint32_t P1,
                                              uint32_t lane) {
         const uint32_t lo = max(P0, e0), hi = min(P1, e1);
-        sb0 = lo < hi ? (lo - e0) / 512 : 0;
+        const uint32_t sb0 = lo < hi ? (lo - e0) / 512 : 0;
 #pragma unroll
         for (uint32_t s = 0; s < kGemmPre; s++) {
             // sub-blocks lie wholly inside [e0, e1), so the load stays below e1
             if (lo < hi && e0 + 512 * (sb0 + s) < hi)
                 pre[s] = *reinterpret_cast<const uint2 *>(a.sm + chunk_at(sb0 + s, lane));
         }
+    }
+
+    // Sub-block sb of the row block from its sign+mantissa bytes S and the
+    // staged exponents of weights A0 .. P1-1; weights outside [lo, hi) enter
+    // as zeros.
+    __device__ __forceinline__ void sub_block(const KArgs &a, uint32_t sb, uint2 S, uint32_t lo,
+                                              uint32_t hi, uint32_t A0, const uint8_t *ebuf,
+                                              uint32_t lane) {
+        const uint32_t g = chunk_at(sb, lane);
+        // chunk (4 sb + l / 16) * T + 16 nb + l % 16 of the reordered activations
+        const uint16_t *xb = xk + 8 * ((4 * sb + (lane >> 4)) * (16 * NB) + (lane & 15u));
+        uint4 bv[NB];
+        if constexpr (kEarly) {
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) bv[nb] = *reinterpret_cast<const uint4 *>(xb + 8 * 16 * nb);
+        }
+        const uint32_t base = e0 + 512 * sb;
+        uint2 E;
+        if (base >= lo && base + 512 <= hi) {  // wave-uniform: the tile holds it all
+            E = *reinterpret_cast<const uint2 *>(ebuf + (g - A0));
+        } else {
+            // held in part: a chunk wholly outside the tile reads a clamped
+            // staging address; the sm and exponent bytes of the weights
+            // outside [lo, hi) are cleared, which makes those weights zero
+            E = *reinterpret_cast<const uint2 *>(ebuf + (g < A0 ? 0u : min(g - A0, a.exp_cap - 8)));
+            const uint32_t ua = min(uint32_t(max(int32_t(lo - g), 0)), 8u);
+            const uint32_t ub = min(uint32_t(max(int32_t(hi - g), 0)), 8u);
+            const uint32_t wd = ub > ua ? ub - ua : 0u;
+            const uint64_t m = wd >= 8 ? ~0ull : ((1ull << (8 * wd)) - 1) << ((8 * ua) & 63u);
+            S.x &= uint32_t(m);
+            S.y &= uint32_t(m >> 32);
+            E.x &= uint32_t(m);
+            E.y &= uint32_t(m >> 32);
+        }
+        uint32_t w[4];
+        assemble4(S.x, E.x, w[0], w[1]);
+        assemble4(S.y, E.y, w[2], w[3]);
+        bf16x8 A;
+        __builtin_memcpy(&A, w, 16);
+        if constexpr (!kEarly) {
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) bv[nb] = *reinterpret_cast<const uint4 *>(xb + 8 * 16 * nb);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            bf16x8 B;
+            __builtin_memcpy(&B, &bv[nb], 16);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[nb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x020, NB, 0);  // the NB vector-memory reads,
+        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // then the NB products
     }
 
     template <int JP, int FMT>
@@ -1238,61 +1292,29 @@ struct GemmEpi {
         const uint32_t lo = max(P0, e0), hi = min(P1, e1);
         if (lo >= hi) return;
         const uint32_t sbA = (lo - e0) / 512, sbB = (hi - 1 - e0) / 512;
-        for (uint32_t sb = sbA; sb <= sbB; sb++) {
-            const uint32_t g = chunk_at(sb, lane);
-            uint2 S;
-            const uint32_t ps = sb - sb0;
-            if (ps < kGemmPre) {
-                S = pre[0];
+        // the first kGemmPre sub-blocks' bytes were prefetched (from sbA)
 #pragma unroll
-                for (uint32_t q = 1; q < kGemmPre; q++) S = ps == q ? pre[q] : S;
-            } else {
-                S = *reinterpret_cast<const uint2 *>(a.sm + g);
-            }
-            // staged exponents of weights A0 .. P1-1; a chunk wholly outside
-            // the tile reads a clamped address and is zeroed below
-            const uint32_t ei = g < A0 ? 0u : min(g - A0, a.exp_cap - 8);
-            const uint2 E = *reinterpret_cast<const uint2 *>(ebuf + ei);
-            uint32_t w[4];
-            assemble4(S.x, E.x, w[0], w[1]);
-            assemble4(S.y, E.y, w[2], w[3]);
-            const uint32_t base = e0 + 512 * sb;
-            if (base < lo || base + 512 > hi) {  // a sub-block the tile holds in part
-#pragma unroll
-                for (uint32_t d = 0; d < 4; d++) {
-                    const uint32_t i = g + 2 * d;
-                    const uint32_t m = (i >= lo && i < hi ? 0x0000FFFFu : 0u) |
-                                       (i + 1 >= lo && i + 1 < hi ? 0xFFFF0000u : 0u);
-                    w[d] &= m;
-                }
-            }
-            bf16x8 A;
-            __builtin_memcpy(&A, w, 16);
-            // chunk (4 sb + l / 16) * T + 16 nb + l % 16 of the reordered activations;
-            // all NB loads are issued before the first product
-            const uint16_t *xb = xk + 8 * ((4 * sb + (lane >> 4)) * (16 * NB) + (lane & 15u));
-            uint4 bv[NB];
-#pragma unroll
-            for (int nb = 0; nb < NB; nb++) bv[nb] = *reinterpret_cast<const uint4 *>(xb + 8 * 16 * nb);
-#pragma unroll
-            for (int nb = 0; nb < NB; nb++) {
-                bf16x8 B;
-                __builtin_memcpy(&B, &bv[nb], 16);
-                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[nb], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x020, NB, 0);  // the NB vector-memory reads,
-            __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // then the NB products
+        for (uint32_t s = 0; s < kGemmPre; s++) {
+            if (sbA + s > sbB) return;
+            sub_block(a, sbA + s, pre[s], lo, hi, A0, ebuf, lane);
         }
+        for (uint32_t sb = sbA + kGemmPre; sb <= sbB; sb++)
+            sub_block(a, sb, *reinterpret_cast<const uint2 *>(a.sm + chunk_at(sb, lane)), lo, hi, A0,
+                      ebuf, lane);
     }
 };
 
+// Occupancy is held to that of the accumulators plus the decode's registers
+// (8, 8, 7 and 6 waves per SIMD for 1-4 token groups; without the cap the
+// compiler spent registers that cost a step in occupancy, 4% at 64 tokens).
 // One workgroup per 16-row block and K segment (longest segments first, in
 // the XCD-grouped order).  The segment's tiles are found in block_out_pos;
 // each wave takes every fourth.  Matrices far wider than the narrowest had
 // whole row blocks take up to 3.5 times as long as the rest (the 70B
 // down projection), which left a tail of few, long workgroups.
 template <int NB>
-__global__ __launch_bounds__(kThreads) void df11_decode_gemm(KArgs a, GemmDesc g, const uint16_t *xs,
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(NB <= 2 ? 8 : NB == 3 ? 7 : 6))) void df11_decode_gemm(KArgs a, GemmDesc g, const uint16_t *xs,
                                                              float *y, float *part) {
     const uint32_t mb = xcd_grouped(blockIdx.x);
     if (mb >= g.mb0[DF11_GEMV_MAX_TENSORS]) return;  // uniform: the grid is rounded up
@@ -1309,7 +1331,6 @@ __global__ __launch_bounds__(kThreads) void df11_decode_gemm(KArgs a, GemmDesc g
     epi.cols = cols;
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) epi.acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    epi.sb0 = 0;
     // tiles holding e0 and e1 - 1 (bop[0] = 0 <= e0 < e1 <= N = bop[n_tiles]
     // for a valid unit; a corrupt bop only yields other tiles in range)
     const uint32_t *bop = a.bop;
