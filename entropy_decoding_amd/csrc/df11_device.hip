@@ -1022,7 +1022,8 @@ struct GemvEpi {
                 sb = ok && wrapped ? t : sb;
             };
 #pragma unroll
-            for (int j = 0; j < JP; j++) pass(j, smv[j]);
+            for (int j = 0; j < JP; j++)
+                if (j < passes) pass(j, smv[j]);
             for (uint32_t j = JP; j < passes; j++) {
                 const uint32_t c = min(lane + 64 * j, n8 - 1);
                 pass(j, *reinterpret_cast<const uint2 *>(sm0 + 8 * c));
