@@ -138,6 +138,7 @@ def test_random_multi_tensor_units(seed):
     u = Unit(tensors, (64, 256, 512)[seed % 3])
     out = check_identity(u, f"random seed={seed}")
     check_sampled_tiles(u, out, 8, seed)
+    check_window_counts(u, oracle.exponents(_cat(tensors)), f"random seed={seed}")
     offs = u.hs.tensor_offsets
     for k in range(len(tensors)):
         if offs[k] % 8:
@@ -154,7 +155,9 @@ def test_random_multi_tensor_units(seed):
 def test_tiny_and_ragged_sizes(n):
     rng = np.random.default_rng(n)
     w = ((rng.standard_normal(n).astype(np.float32) * 0.02).view(np.uint32) >> 16).astype(np.uint16)
-    check_identity(Unit([w]), f"n={n}")
+    u = Unit([w])
+    check_identity(u, f"n={n}")
+    check_window_counts(u, oracle.exponents(w), f"n={n}")
 
 
 def test_single_exponent_one_bit_codes():
