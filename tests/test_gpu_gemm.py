@@ -213,6 +213,28 @@ def test_gemm_argument_errors_and_corruption():
         assert int(st.item()) == ed.DF11_E_CORRUPT
 
 
+def test_gemm_split_matrix_corruption_is_reported_and_other_matrices_exact():
+    """A corrupt block_out_pos entry inside a matrix split into three K
+    segments is reported; the unsplit matrix before it, whose tiles are
+    intact, keeps its exact products."""
+    rng = np.random.default_rng(12)
+    shapes = [(16, 4096), (16, 12288)]
+    u = _int_unit(rng, shapes)
+    n = 16
+    x = _bf16(rng.integers(-3, 4, sum(n * c for _, c in shapes)).astype(np.float32))
+    bad = u.hs.block_out_pos.copy()
+    t = int(np.searchsorted(bad, 16 * 4096 + 16 * 6000))  # a tile boundary in the split matrix
+    assert bad[t - 1] > 16 * 4096 + 512
+    bad[t] += 3
+    u.ds.block_out_pos.copy_(torch.from_numpy(bad.view(np.uint8)))
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y, code = u.run(x, n, "split corrupt", status=st)
+    assert code == ed.DF11_E_CORRUPT
+    ref = oracle.gemm(np.concatenate(u.tensors), shapes, x, n)
+    first = ref.reshape(-1)[: n * 16]  # y of the first matrix (token-major, 16 rows)
+    assert np.array_equal(y[: n * 16], first)
+
+
 @pytest.mark.parametrize("shapes,split", [([(32, 512), (16, 256)], 0),
                                           ([(16, 4096), (16, 8224)], 3)])
 def test_gemm_scratch_needs_no_initialisation_and_is_checked(shapes, split):
