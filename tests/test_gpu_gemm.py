@@ -127,7 +127,7 @@ def test_gemm_gaussian_data_within_the_bound_and_deterministic():
     assert np.all(err <= _bound(tensors, shapes, x, n) + 1e-30)
 
 
-@pytest.mark.parametrize("n", [16, 64])
+@pytest.mark.parametrize("n", [16, 32, 48, 64])
 def test_gemm_split_rows_integer_exact_and_gaussian_bound(n):
     """Matrices 3.25 and 2.02 times wider than the narrowest (4096 columns)
     are split into K segments of 104 and 87/87/85 sub-blocks: integer data
