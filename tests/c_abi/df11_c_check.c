@@ -140,7 +140,19 @@ int main(void) {
     CHECK(df11_decompress_tensor(&ds, 0, d_out, d_status, NULL) == DF11_OK);
     CHECK(hipMemcpy(out, d_out, 2 * numel[0], hipMemcpyDeviceToHost) == hipSuccess);
     CHECK(memcmp(out, w[0], numel[0] * 2) == 0);
-    printf("gpu: decompress_block and decompress_tensor bit-exact\n");
+    /* the first decode phase alone: each tile's window counts add up to its
+       block_out_pos difference */
+    uint32_t *d_counts;
+    CHECK(hipMalloc((void **)&d_counts, 4 * sz.n_windows) == hipSuccess);
+    CHECK(df11_window_counts(&ds, d_counts, NULL) == DF11_OK);
+    uint32_t *counts = (uint32_t *)malloc(4 * sz.n_windows);
+    CHECK(hipMemcpy(counts, d_counts, 4 * sz.n_windows, hipMemcpyDeviceToHost) == hipSuccess);
+    for (uint64_t t = 0; t < sz.n_tiles; t++) {
+        uint64_t c = 0;
+        for (uint64_t j = 64 * t; j < 64 * (t + 1); j++) c += counts[j];
+        CHECK(c == (uint64_t)hs.block_out_pos[t + 1] - hs.block_out_pos[t]);
+    }
+    printf("gpu: decompress_block and decompress_tensor bit-exact; window counts consistent\n");
 #endif
     return 0;
 }
