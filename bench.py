@@ -81,27 +81,34 @@ def cpu_name() -> str:
     return platform.processor() or "unknown"
 
 
-def cpu_baseline(tensors, seconds_budget: float = 30.0):
-    """The oracle's bit-serial decode on this host: one thread per tensor (each
-    tensor encoded by the oracle with the unit's codebook first, untimed)."""
+def cpu_baseline(tensors):
+    """The oracle as it stands, on this host's cores, after the GPU timing.
+
+    Three figures from one oracle encoding of the whole unit (the unit's
+    codebook, the plain bit-serial encoder): the encode itself on one thread,
+    a bit-serial decode of the whole unit on one thread, and one thread per
+    tensor decoding from the tensor start bits the oracle's encoder records.
+    GB/s are BF16 bytes (2 per weight) per second.  `value` is the
+    thread-per-tensor decode."""
     import oracle
 
+    n = sum(t.size for t in tensors)
     ocb = oracle.codebook(tensors)
-    encs = [None] * len(tensors)
-
-    def enc(i):
-        encs[i] = oracle.encode([tensors[i]], ocb)
-
-    ths = [threading.Thread(target=enc, args=(i,)) for i in range(len(tensors))]
-    for t in ths:
-        t.start()
-    for t in ths:
-        t.join()
+    t0 = time.perf_counter()
+    enc = oracle.encode(tensors, ocb)
+    t_enc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    whole = oracle.decode(enc.stream, 0, enc.total_bits, ocb.lens, enc.sm)
+    t_one = time.perf_counter() - t0
+    flat = np.concatenate([np.asarray(t).reshape(-1) for t in tensors])
+    assert np.array_equal(whole, flat), "oracle decode is not lossless"
+    del whole
     outs = [None] * len(tensors)
+    offs = np.cumsum([0] + [t.size for t in tensors])
 
     def dec(i):
-        e = encs[i]
-        outs[i] = oracle.decode(e.stream, 0, e.total_bits, ocb.lens, e.sm)
+        outs[i] = oracle.decode(enc.stream, enc.tensor_start_bits[i], enc.tensor_start_bits[i + 1],
+                                ocb.lens, enc.sm[offs[i]:offs[i + 1]])
 
     ths = [threading.Thread(target=dec, args=(i,)) for i in range(len(tensors))]
     t0 = time.perf_counter()
@@ -109,15 +116,52 @@ def cpu_baseline(tensors, seconds_budget: float = 30.0):
         t.start()
     for t in ths:
         t.join()
-    dt = time.perf_counter() - t0
+    t_par = time.perf_counter() - t0
     for o, t in zip(outs, tensors):
-        assert np.array_equal(o, t), "oracle decode is not lossless"
-    n = sum(t.size for t in tensors)
-    return {"value": round(2 * n / dt / 1e9, 4), "unit": "GB/s", "cores": len(tensors),
-            "kind": "oracle",
-            "sample": f"all {len(tensors)} tensors of the unit ({n} weights), one thread per "
-                      f"tensor, bit-serial canonical decode, {dt:.2f} s wall on {cpu_name()} "
-                      f"(nproc={os.cpu_count()})"}
+        assert np.array_equal(o, np.asarray(t).reshape(-1)), "oracle decode is not lossless"
+    host, nproc = cpu_name(), os.cpu_count()
+    gbs = lambda dt: round(2 * n / dt / 1e9, 4)
+    return {"value": gbs(t_par), "unit": "GB/s", "cores": len(tensors), "kind": "oracle",
+            "sample": f"host {host}, nproc {nproc}, {len(tensors)} threads: the whole unit "
+                      f"({n} weights, {len(tensors)} tensors), one thread per tensor decoding "
+                      f"bit-serially from the oracle's tensor start bits, {t_par:.2f} s wall; "
+                      f"one thread over the whole unit {t_one:.2f} s; oracle encode on one "
+                      f"thread {t_enc:.2f} s",
+            "host": host, "nproc": nproc,
+            "decode_one_thread": {"value": gbs(t_one), "unit": "GB/s", "cores": 1,
+                                  "seconds": round(t_one, 3)},
+            "encode_one_thread": {"value": gbs(t_enc), "unit": "GB/s of BF16 input", "cores": 1,
+                                  "seconds": round(t_enc, 3)}}
+
+
+def settle(step, torch, ms: float = 100.0, max_launches: int = 5000):
+    """Runs step() until the GPU has been kept busy for `ms` milliseconds.
+
+    An idle MI355X sits at a low shader clock (157 MHz read by rocm-smi before
+    a run) and ramps up only over tens of milliseconds of work: on the 70B
+    block, five warm-up launches left the first timed launches at 0.63-0.65 ms
+    against 0.537 ms once settled.  This runs before the warm-up steps, untimed,
+    and its length is reported."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < max_launches:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            break
+    return {"launches": n, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
+
+
+def log_steps(name, kms):
+    """Per-step kernel times on stderr: the first and last steps, so that a
+    run whose early steps are slower than its late ones shows it."""
+    k = np.asarray(kms)
+    head = " ".join(f"{v:.4f}" for v in k[:8])
+    tail = " ".join(f"{v:.4f}" for v in k[-8:])
+    log(f"[bench] {name}: step ms first [{head}] last [{tail}] "
+        f"min {k.min():.4f} p50 {np.percentile(k, 50):.4f} max {k.max():.4f}")
 
 
 def run_unit(name, tensors, args, torch, ed):
@@ -141,6 +185,8 @@ def run_unit(name, tensors, args, torch, ed):
     flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if small else None
     sink = torch.zeros((), dtype=torch.int32, device=dev)
 
+    settled = settle(lambda: ed.df11_decompress_block(ds, out, status, stream), torch,
+                     args.settle_ms)
     for _ in range(args.warmup):
         ed.df11_decompress_block(ds, out, status, stream)
     torch.cuda.synchronize()
@@ -158,6 +204,7 @@ def run_unit(name, tensors, args, torch, ed):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    log_steps(name, kms)
 
     st = int(status.item())
     if args.format == "bf16":
@@ -173,7 +220,7 @@ def run_unit(name, tensors, args, torch, ed):
     return {
         "name": name, "n": n, "hs": hs, "cb": cb, "kernel_ms": kms, "wall_s": wall,
         "alg_bytes": alg, "exact": exact, "status": st, "payload_bpw": payload,
-        "total_bpw": total_bits, "flushed": small,
+        "total_bpw": total_bits, "flushed": small, "settle": settled,
     }
 
 
@@ -185,6 +232,10 @@ def main():
     ap.add_argument("--config", default="2")
     ap.add_argument("--tile-windows", type=int, default=64, choices=(64, 256, 512))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="keep the GPU busy this long before the warm-up steps (clock ramp)")
+    ap.add_argument("--no-extra-configs", dest="extra_configs", action="store_false",
+                    help="skip timing configs 0, 1, 3a-c after the 70B block")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes instead "
                          "(the achievable-bandwidth reference and the counter calibration)")
@@ -234,14 +285,7 @@ def main():
     if len(cfg.units) != 1:
         return stream_units(cfg, args, torch, ed, sw)
     unit = cfg.units[0]
-    t0 = time.perf_counter()
-    if args.format == "bf16":
-        tensors = sw.gen_unit(unit)
-        workload = cfg.name
-    else:
-        tensors = sw.gen_unit_fp8(unit, args.format.split("_")[1])
-        workload = f"{cfg.name}_{args.format}"
-    log(f"[bench] generated {workload} ({unit.numel} weights) in {time.perf_counter() - t0:.1f} s")
+    tensors, workload = gen_workload(unit, cfg, args, sw)
     r = run_unit(workload, tensors, args, torch, ed)
     out_bytes = 2 if args.format == "bf16" else 1
     kms = r["kernel_ms"]
@@ -264,12 +308,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32",
+        "dtype": args.format,
         "data": "synthetic",
         "config": {
             "workload": workload,
             "n_weights": n,
             "layout": f"T{args.tile_windows}xB8",
+            "arithmetic": "integer (bit-exact decode; no floating point)",
             "bit_exact": bool(r["exact"]),
             "bits_per_weight_payload": round(r["payload_bpw"], 4),
             "bits_per_weight_total": round(r["total_bpw"], 4),
@@ -277,6 +322,7 @@ def main():
             "kernel_ms_p50": round(float(np.percentile(kms, 50)), 4),
             "kernel_ms_p99": round(float(np.percentile(kms, 99)), 4),
             "caches_flushed_between_steps": r["flushed"],
+            "settle_before_warmup": r["settle"],
         },
         "roofline": {
             "bound": "hbm",
@@ -286,13 +332,64 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
         },
+        "system": system_info(torch),
     }
+    del r
+    if args.extra_configs and args.config == "2" and args.format == "bf16":
+        line["other_configs"] = other_configs(args, torch, ed, sw)
     if not args.no_cpu_baseline and args.format == "bf16":
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(tensors)
     print(json.dumps(line), flush=True)
-    if not r["exact"]:
+    if not line["config"]["bit_exact"] or not all(
+            c["bit_exact"] for c in line.get("other_configs", {}).values()):
         sys.exit(1)
+
+
+def gen_workload(unit, cfg, args, sw):
+    t0 = time.perf_counter()
+    if args.format == "bf16":
+        tensors = sw.gen_unit(unit)
+        workload = cfg.name
+    else:
+        tensors = sw.gen_unit_fp8(unit, args.format.split("_")[1])
+        workload = f"{cfg.name}_{args.format}"
+    log(f"[bench] generated {workload} ({unit.numel} weights) in {time.perf_counter() - t0:.1f} s")
+    return tensors, workload
+
+
+def system_info(torch) -> dict:
+    p = torch.cuda.get_device_properties(0)
+    return {"gpu": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+
+
+def other_configs(args, torch, ed, sw) -> dict:
+    """The single-unit configurations besides the 70B block, in the same
+    process after it: each timed like the headline (settle, warm-up, timed
+    steps with the caches evicted between steps) and compared with the
+    original bits."""
+    res = {}
+    for k in ("0", "1", "3a", "3b", "3c"):
+        cfg = sw.config(k)
+        unit = cfg.units[0]
+        tensors, name = gen_workload(unit, cfg, args, sw)
+        r = run_unit(name, tensors, args, torch, ed)
+        kms = r["kernel_ms"]
+        ach = r["alg_bytes"] / (float(kms.mean()) * 1e-3) / 1e9
+        res[name] = {
+            "n_weights": r["n"], "bit_exact": bool(r["exact"]),
+            "bf16_out_gbs": round(2 * r["n"] / (float(kms.mean()) * 1e-3) / 1e9, 1),
+            "kernel_ms_p50": round(float(np.percentile(kms, 50)), 4),
+            "kernel_ms_p99": round(float(np.percentile(kms, 99)), 4),
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "bits_per_weight_payload": round(r["payload_bpw"], 4),
+            "bits_per_weight_total": round(r["total_bpw"], 4),
+            "caches_flushed_between_steps": r["flushed"],
+        }
+        del r, tensors
+        torch.cuda.empty_cache()
+    return res
 
 
 def copy_reference(args, torch):
@@ -339,6 +436,15 @@ def stream_units(cfg, args, torch, ed, sw):
     out = torch.empty(nmax, dtype=torch.bfloat16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    # a unit is read again only after the rest of the pass: when a whole pass
+    # moves under 1 GiB, its data could still sit in the 256 MB last-level
+    # cache, so the caches are evicted before every launch by reading 1 GiB
+    # (outside the timed events), as for the single-unit configs
+    pass_bytes = sum(algorithmic_bytes(u[2], u[3]) for u in units)
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if pass_bytes < (1 << 30) else None
+    sink = torch.zeros((), dtype=torch.int32, device=dev)
+    settled = settle(lambda: ed.df11_decompress_block(units[0][1], out, status, stream), torch,
+                     args.settle_ms)
     for _ in range(args.warmup):
         for u in units:
             ed.df11_decompress_block(u[1], out, status, stream)
@@ -349,6 +455,8 @@ def stream_units(cfg, args, torch, ed, sw):
     t0 = time.perf_counter()
     for p in range(passes):
         for i, u in enumerate(units):
+            if flush is not None:
+                torch.amax(flush, dim=0, out=sink)
             ev[p][i][0].record(stream)
             ed.df11_decompress_block(u[1], out, status, stream)
             ev[p][i][1].record(stream)
@@ -369,12 +477,14 @@ def stream_units(cfg, args, torch, ed, sw):
     blocks = lat[:, [i for i, u in enumerate(units) if u[0].name.startswith("block")]]
     avg_pass_ms = float(lat.sum(axis=1).mean())
     achieved = alg / (avg_pass_ms * 1e-3) / 1e9
+    # with flushes in between, the job's time is the sum of the launches' times
+    job_s = float(lat.sum()) * 1e-3 if flush is not None else wall
     line = {
         "metric": "decompressed BF16 GB/s",
-        "value": round(2 * n_total * passes / wall / 1e9, 2),
+        "value": round(2 * n_total * passes / job_s / 1e9, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": passes, "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / passes, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "ms_per_step": round(job_s * 1e3 / passes, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {
             "workload": cfg.name, "n_weights": n_total, "units": len(units),
             "layout": f"T{args.tile_windows}xB8", "bit_exact": bool(exact),
@@ -384,6 +494,8 @@ def stream_units(cfg, args, torch, ed, sw):
             "block_ms_p99": round(float(np.percentile(blocks, 99)), 4) if blocks.size else None,
             "per_unit_ms_mean": {u[0].name: round(float(lat[:, i].mean()), 4)
                                  for i, u in enumerate(units)},
+            "caches_flushed_between_steps": flush is not None,
+            "settle_before_warmup": settled,
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
@@ -434,6 +546,7 @@ def encode_bench(args, torch, ed, sw):
             ed.FORMATS[fmt], ctypes.byref(cb), ctypes.c_void_p(w.data_ptr()), n, args.tile_windows,
             8, ctypes.byref(sz), ctypes.byref(out), sh))
 
+    settle(lambda: (hist(), enc()), torch, args.settle_ms)
     for _ in range(max(1, min(args.warmup, 10))):
         hist()
         enc()
@@ -466,7 +579,7 @@ def encode_bench(args, torch, ed, sw):
     line = {
         "metric": "GPU encode GB/s (input weights)", "value": round(in_bytes / (total_ms * 1e-3) / 1e9, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "higher_is_better": True,
-        "dtype": "u32", "data": "synthetic",
+        "dtype": fmt, "data": "synthetic",
         "config": {"workload": cfg.name if fmt == "bf16" else f"{cfg.name}_{fmt}", "n_weights": n,
                    "layout": f"T{args.tile_windows}xB8", "byte_exact_vs_host_encoder": bool(exact)},
         "device_ms": {"histogram": round(float(h_ms.mean()), 4), "encode": round(float(e_ms.mean()), 4),
@@ -560,6 +673,8 @@ def pipeline_bench(args, torch, ed, sw):
         return (time.perf_counter() - t) * 1e3 / (passes * nb)
 
     passes = max(1, args.steps // 5)
+    settle(lambda: ed.df11_decompress_block(blocks[0][1], bufs[0], status, main_s), torch,
+           args.settle_ms)
     pipe = ed.Pipeline(decode_s, 2)
     for _, ds, _, _ in blocks[:2]:
         ed.df11_decompress_block(ds, bufs[0], status, main_s)
@@ -607,7 +722,7 @@ def pipeline_bench(args, torch, ed, sw):
         "metric": "pipelined block time (decompress next block while the GEMV reads this one)",
         "value": g["pipelined_ms"], "unit": "ms per block", "n_gpus": 1,
         "steps": passes, "warmup": max(1, min(args.warmup, 3)), "higher_is_better": False,
-        "vs_baseline": None, "dtype": "u32+f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16 decode + f32 GEMV", "data": "synthetic",
         "config": {"workload": "llama3_8b_32_blocks", "blocks": nb, "n_weights_per_block": n,
                    "slots": 2, "layout": f"T{args.tile_windows}xB8", "bit_exact": bool(exact)},
         "consumers": results,
@@ -685,6 +800,7 @@ def fused_bench(args, torch, ed, sw):
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in ev])
 
+    settle(fused, torch, args.settle_ms)
     res = {name: timed(fn) for name, fn in
            (("fused", fused), ("decompress_then_gemv", sequential), ("bf16_gemv", resident))}
     ok = int(status.item()) == 0 and torch.equal(buf, w_res)
@@ -716,7 +832,7 @@ def fused_bench(args, torch, ed, sw):
         "metric": "fused decompress+GEMV time per block",
         "value": round(float(f.mean()), 4), "unit": "ms per block", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
-        "vs_baseline": None, "dtype": "u32+f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16 x f32 -> f32", "data": "synthetic",
         "config": {"workload": cfg.name, "n_weights": n, "layout": "T64xB8",
                    "within_rounding_bound": bool(ok), "caches_flushed_between_steps": small},
         "ms": {k: {"mean": round(float(v.mean()), 4), "p50": round(float(np.percentile(v, 50)), 4)}
@@ -812,6 +928,7 @@ def fused_gemm_bench(args, torch, ed, sw):
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in ev])
 
+    settle(fused, torch, args.settle_ms)
     res = {name: timed(fn) for name, fn in
            (("fused", fused), ("decompress_then_gemm", sequential), ("bf16_gemm", resident))}
     ok = int(status.item()) == 0 and torch.equal(buf.view(torch.int16), w_res.view(torch.int16))

@@ -199,6 +199,9 @@ def _load():
                                                _u64p, ctypes.c_uint64, ctypes.c_uint32,
                                                ctypes.c_uint32, ctypes.POINTER(df11_sizes)]
     L.df11_histogram_device.argtypes = [ctypes.c_uint32, vp, ctypes.c_uint64, vp, vp]
+    L.df11_tensor_ranges_from_counts.argtypes = [ctypes.c_uint32, ctypes.POINTER(df11_codebook),
+                                                 _u64p, _u32p, ctypes.c_uint32, ctypes.c_uint32,
+                                                 ctypes.c_uint32, _u64p, _u64p]
     L.df11_encode_device_scratch_bytes.argtypes = [ctypes.c_uint64]
     L.df11_encode_device_scratch_bytes.restype = ctypes.c_uint64
     L.df11_encode_device.argtypes = [ctypes.c_uint32, ctypes.POINTER(df11_codebook), vp,
@@ -212,7 +215,7 @@ def _load():
               L.df11_pipeline_release, L.df11_gemv_bf16, L.df11_build_codebook_from_counts,
               L.df11_encode_size_from_counts, L.df11_histogram_device, L.df11_encode_device,
               L.df11_decompress_gemv, L.df11_gemm_order, L.df11_decompress_gemm,
-              L.df11_window_counts):
+              L.df11_window_counts, L.df11_tensor_ranges_from_counts):
         f.restype = ctypes.c_int
     return L
 
@@ -590,11 +593,15 @@ def df11_decompress_gemm(ds: DeviceStream, layout, n_tokens: int, x, y, scratch=
 # ---------------------------------------------------------------- device encoder
 
 
-def df11_histogram_device(w, fmt: str = "bf16", stream=None):
-    """Exponent histogram of the device tensor ``w`` (uint64[256] on its device)."""
+def df11_histogram_device(w, fmt: str = "bf16", stream=None, counts=None):
+    """Exponent histogram of the device tensor ``w`` (uint64[256] on its device;
+    written into ``counts``, a 256-element 8-byte device tensor, when given)."""
     import torch
 
-    counts = torch.empty(256, dtype=torch.int64, device=w.device)
+    if counts is None:
+        counts = torch.empty(256, dtype=torch.int64, device=w.device)
+    elif counts.numel() != 256 or counts.element_size() != 8 or not counts.is_contiguous():
+        raise ValueError("counts must be 256 contiguous 8-byte elements")
     _check("df11_histogram_device",
            LIB.df11_histogram_device(_format(fmt), ctypes.c_void_p(w.data_ptr()), w.numel(),
                                      ctypes.c_void_p(counts.data_ptr()), _stream_handle(stream)))
@@ -609,72 +616,93 @@ def df11_build_codebook_from_counts(counts) -> df11_codebook:
     return cb
 
 
+def df11_tensor_ranges_from_counts(cb: df11_codebook, counts, last_weights, fmt: str = "bf16",
+                                   tile_windows: int = DEFAULT_TILE_WINDOWS,
+                                   window_bytes: int = DEFAULT_WINDOW_BYTES):
+    """(tensor_offsets uint64[n+1], tensor_tiles uint64[2n]) from per-tensor
+    histograms ``counts`` (n x 256) and the tensors' last weights (n bit patterns)."""
+    c = np.ascontiguousarray(np.asarray(counts), dtype=np.uint64).reshape(-1, 256)
+    n = c.shape[0]
+    last = np.ascontiguousarray(np.asarray(last_weights), dtype=np.uint32).reshape(-1)
+    if last.size != n:
+        raise ValueError("one last weight per tensor")
+    offs = np.zeros(n + 1, dtype=np.uint64)
+    tiles = np.zeros(max(2 * n, 1), dtype=np.uint64)
+    _check("df11_tensor_ranges_from_counts",
+           LIB.df11_tensor_ranges_from_counts(_format(fmt), ctypes.byref(cb), c.ctypes.data_as(_u64p),
+                                              last.ctypes.data_as(_u32p), n, tile_windows,
+                                              window_bytes, offs.ctypes.data_as(_u64p),
+                                              tiles.ctypes.data_as(_u64p)))
+    return offs, tiles[: 2 * n]
+
+
 def encode_on_device(tensors, fmt: str = "bf16", tile_windows: int = DEFAULT_TILE_WINDOWS,
                      window_bytes: int = DEFAULT_WINDOW_BYTES, stream=None):
     """Compress device tensors (16-bit for BF16, 8-bit for FP8) into a
     DeviceStream without moving the weights to the host: per-tensor device
     histograms, the codebook built on the host from them, then
-    df11_encode_device on the concatenated unit.  Returns (DeviceStream, codebook)."""
+    df11_encode_device on the concatenated unit.  Every allocation, copy and
+    launch is ordered on ``stream`` (a torch stream or a raw hipStream_t; the
+    current stream when None), and the call returns once that stream has
+    finished the encoding.  Returns (DeviceStream, codebook)."""
     import torch
 
+    if stream is None:
+        st = torch.cuda.current_stream()
+    elif isinstance(stream, torch.cuda.Stream):
+        st = stream
+    else:
+        st = torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
     size = 2 if fmt == "bf16" else 1
-    flat = []
     for t in tensors:
         if t.element_size() != size:
             raise TypeError(f"{fmt} tensors must have {8 * size}-bit elements")
-        flat.append(t.reshape(-1).view(torch.int16 if size == 2 else torch.uint8))
-    unit = torch.cat(flat) if len(flat) != 1 else flat[0].contiguous()
-    n = unit.numel()
-    per = [df11_histogram_device(t.contiguous(), fmt, stream) for t in flat]
-    per_h = [c.cpu().numpy().view(np.uint64) for c in per]
-    counts = np.sum(per_h, axis=0).astype(np.uint64) if per_h else np.zeros(256, np.uint64)
-    cb = df11_build_codebook_from_counts(counts)
-    sz = df11_sizes()
-    _check("df11_encode_size_from_counts",
-           LIB.df11_encode_size_from_counts(_format(fmt), ctypes.byref(cb),
-                                            counts.ctypes.data_as(_u64p), n, tile_windows,
-                                            window_bytes, ctypes.byref(sz)))
-    dev = unit.device
-    st = torch.empty(sz.stream_bytes, dtype=torch.uint8, device=dev)
-    sm = torch.empty(sz.sm_bytes, dtype=torch.uint8, device=dev)
-    gaps = torch.empty(max(16, sz.n_windows), dtype=torch.uint8, device=dev)
-    bop = torch.empty(sz.bop_entries, dtype=torch.int32, device=dev)
-    mx = torch.empty(4, dtype=torch.int32, device=dev)
-    nbytes = int(LIB.df11_encode_device_scratch_bytes(n))
-    scratch = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
-    sp = scratch.data_ptr()
-    out = df11_device_encode(st.data_ptr(), sm.data_ptr(), gaps.data_ptr(), bop.data_ptr(),
-                             mx.data_ptr(), (sp + 255) // 256 * 256, nbytes)
-    _check("df11_encode_device",
-           LIB.df11_encode_device(_format(fmt), ctypes.byref(cb), ctypes.c_void_p(unit.data_ptr()),
-                                  n, tile_windows, window_bytes, ctypes.byref(sz),
-                                  ctypes.byref(out), _stream_handle(stream)))
-    # per-tensor offsets and tile ranges, as df11_encode computes them
-    lens = np.ctypeslib.as_array(cb.code_len).astype(np.uint64)
-    tshift = (8 * window_bytes * tile_windows).bit_length() - 1  # log2 of tile bits
-    offs = np.zeros(len(flat) + 1, dtype=np.uint64)
-    tiles = np.zeros(max(2, 2 * len(flat)), dtype=np.uint64)
-    g = bit = 0
-    for k, (t, c) in enumerate(zip(flat, per_h)):
-        offs[k] = g
-        bits_k = int((c * lens).sum())
-        tiles[2 * k] = bit >> tshift
-        if t.numel():
-            last = int(t[-1].item()) & (0xFFFF if size == 2 else 0xFF)
-            sym = (last >> 7) & 0xFF if fmt == "bf16" else \
-                ((last >> 3) & 0xF if fmt == "fp8_e4m3" else (last >> 2) & 0x1F)
-            tiles[2 * k + 1] = ((bit + bits_k - int(lens[sym])) >> tshift) + 1
-        else:
-            tiles[2 * k + 1] = tiles[2 * k]
-        g += t.numel()
-        bit += bits_k
-    offs[len(flat)] = n
-    torch.cuda.synchronize(dev)
+    cur = torch.cuda.current_stream()
+    with torch.cuda.stream(st):
+        if st != cur:
+            st.wait_stream(cur)  # the work that wrote the tensors comes first
+        flat = [t.reshape(-1).view(torch.int16 if size == 2 else torch.uint8).contiguous()
+                for t in tensors]
+        unit = torch.cat(flat) if len(flat) != 1 else flat[0]
+        n = unit.numel()
+        dev = unit.device
+        per = torch.zeros((max(len(flat), 1), 256), dtype=torch.int64, device=dev)
+        lasts = torch.zeros(max(len(flat), 1), dtype=torch.int32, device=dev)
+        for k, t in enumerate(flat):
+            if t.numel():
+                df11_histogram_device(t, fmt, st, per[k])
+                lasts[k] = t[-1].to(torch.int32)
+        per_h = per.cpu().numpy().view(np.uint64)[: len(flat)]  # waits for st
+        lasts_h = lasts.cpu().numpy().view(np.uint32)[: len(flat)] & (0xFFFF if size == 2 else 0xFF)
+        counts = per_h.sum(axis=0, dtype=np.uint64) if len(flat) else np.zeros(256, np.uint64)
+        cb = df11_build_codebook_from_counts(counts)
+        sz = df11_sizes()
+        _check("df11_encode_size_from_counts",
+               LIB.df11_encode_size_from_counts(_format(fmt), ctypes.byref(cb),
+                                                counts.ctypes.data_as(_u64p), n, tile_windows,
+                                                window_bytes, ctypes.byref(sz)))
+        offs, tiles = df11_tensor_ranges_from_counts(cb, per_h, lasts_h, fmt, tile_windows,
+                                                     window_bytes)
+        stm = torch.empty(sz.stream_bytes, dtype=torch.uint8, device=dev)
+        sm = torch.empty(sz.sm_bytes, dtype=torch.uint8, device=dev)
+        gaps = torch.empty(max(16, sz.n_windows), dtype=torch.uint8, device=dev)
+        bop = torch.empty(sz.bop_entries, dtype=torch.int32, device=dev)
+        mx = torch.empty(4, dtype=torch.int32, device=dev)
+        nbytes = int(LIB.df11_encode_device_scratch_bytes(n))
+        scratch = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+        sp = scratch.data_ptr()
+        out = df11_device_encode(stm.data_ptr(), sm.data_ptr(), gaps.data_ptr(), bop.data_ptr(),
+                                 mx.data_ptr(), (sp + 255) // 256 * 256, nbytes)
+        _check("df11_encode_device",
+               LIB.df11_encode_device(_format(fmt), ctypes.byref(cb),
+                                      ctypes.c_void_p(unit.data_ptr()), n, tile_windows,
+                                      window_bytes, ctypes.byref(sz), ctypes.byref(out),
+                                      _stream_handle(st)))
+        max_tile = int(mx.cpu()[0])  # waits for st: the arrays are complete
     hs = HostStream(np.zeros(0, np.uint8), np.zeros(0, np.uint8), np.zeros(sz.n_windows, np.uint8),
-                    np.zeros(sz.bop_entries, np.uint32), offs, tiles[: 2 * len(flat)],
-                    tile_windows, window_bytes, int(mx[0].item()), n, int(sz.total_bits),
-                    int(sz.n_tiles), _format(fmt))
-    ds = DeviceStream(hs, cb, dev, arrays=(st, sm, gaps, bop))
+                    np.zeros(sz.bop_entries, np.uint32), offs, tiles, tile_windows, window_bytes,
+                    max_tile, n, int(sz.total_bits), int(sz.n_tiles), _format(fmt))
+    ds = DeviceStream(hs, cb, dev, arrays=(stm, sm, gaps, bop))
     return ds, cb
 
 

@@ -1441,7 +1441,12 @@ int prepare(const df11_device_stream *s, KArgs &a) {
     const uint64_t tile_bits = uint64_t(64) * s->tile_windows;
     if (s->n_tiles != (s->total_bits + tile_bits - 1) / tile_bits) return DF11_E_INVALID;
     if (s->n_tiles >= (uint64_t(1) << 32)) return DF11_E_INVALID;
-    if (s->n_weights == 0) return DF11_OK;
+    // an empty unit has no stream; a descriptor that claims tiles or bits for
+    // it is inconsistent and must not reach a launch (its pointers may be null)
+    if (s->n_weights == 0) return s->n_tiles == 0 && s->total_bits == 0 ? DF11_OK : DF11_E_INVALID;
+    // every weight has a code of 1 .. 32 bits
+    if (s->total_bits < s->n_weights || s->total_bits > uint64_t(DF11_MAX_CODE_LEN) * s->n_weights)
+        return DF11_E_INVALID;
     if (!s->stream || !s->sm || !s->gaps || !s->block_out_pos || !s->tables)
         return DF11_E_INVALID;
     if (!aligned(s->stream, 16) || !aligned(s->sm, 16) || !aligned(s->tables, 16) ||

@@ -470,6 +470,29 @@ void encode_piece(const df11_codebook *cb, const Piece &pc, uint64_t pos, uint64
     po.last_window = last_window;
 }
 
+// Element offsets and tile ranges of the unit's tensors: tensor k holds
+// numel[k] weights whose codes take bits[k] bits, and its last weight's symbol
+// is last_sym[k].  Its tiles run from the one holding its first code start to
+// the one holding its last.
+void tensor_ranges(const df11_codebook *cb, const uint64_t *numel, const uint64_t *bits,
+                   const uint32_t *last_sym, uint32_t n_tensors, int tshift,
+                   uint64_t *tensor_offsets, uint64_t *tensor_tiles) {
+    uint64_t g = 0, bit = 0;
+    for (uint32_t k = 0; k < n_tensors; k++) {
+        tensor_offsets[k] = g;
+        tensor_tiles[2 * k] = bit >> tshift;
+        if (numel[k]) {
+            const uint64_t last_start = bit + bits[k] - cb->code_len[last_sym[k] & 0xFFu];
+            tensor_tiles[2 * k + 1] = (last_start >> tshift) + 1;
+        } else {
+            tensor_tiles[2 * k + 1] = tensor_tiles[2 * k];
+        }
+        g += numel[k];
+        bit += bits[k];
+    }
+    tensor_offsets[n_tensors] = g;
+}
+
 }  // namespace
 
 extern "C" {
@@ -532,6 +555,45 @@ int df11_encode_size_from_counts(uint32_t format, const df11_codebook *cb, const
     for (int s = 0; s < kSyms; s++) n += counts[s];
     if (n != n_weights) return DF11_E_INVALID;
     return sizes_from_counts(format, cb, counts, n, tile_windows, window_bytes, out);
+}
+
+int df11_tensor_ranges_from_counts(uint32_t format, const df11_codebook *cb,
+                                   const uint64_t *counts, const uint32_t *last_weights,
+                                   uint32_t n_tensors, uint32_t tile_windows,
+                                   uint32_t window_bytes, uint64_t *tensor_offsets,
+                                   uint64_t *tensor_tiles) {
+    try {
+        if (!cb || !valid_codebook(cb) || !valid_layout(tile_windows, window_bytes) ||
+            !valid_format_layout(format, tile_windows) || !tensor_offsets ||
+            (n_tensors && (!counts || !last_weights || !tensor_tiles)))
+            return DF11_E_INVALID;
+        std::vector<uint64_t> numel(n_tensors, 0), bits(n_tensors, 0);
+        std::vector<uint32_t> last_sym(n_tensors, 0);
+        uint64_t n = 0;
+        for (uint32_t k = 0; k < n_tensors; k++) {
+            const uint64_t *c = counts + uint64_t(k) * kSyms;
+            for (int s = 0; s < kSyms; s++) {
+                if (c[s] && !cb->code_len[s]) return DF11_E_SYMBOL;
+                numel[k] += c[s];
+                bits[k] += c[s] * cb->code_len[s];
+            }
+            n += numel[k];
+            if (!numel[k]) continue;
+            bool ok = with_format(format, [&](auto fm) {
+                using Fm = decltype(fm);
+                last_sym[k] = Fm::sym(typename Fm::T(last_weights[k]));
+            });
+            if (!ok) return DF11_E_INVALID;
+            if (!c[last_sym[k]]) return DF11_E_INVALID;  // the last weight is not counted
+        }
+        if (n >= (uint64_t(1) << 32)) return DF11_E_INVALID;
+        const int tshift = log2u(uint64_t(8) * window_bytes) + log2u(tile_windows);
+        tensor_ranges(cb, numel.data(), bits.data(), last_sym.data(), n_tensors, tshift,
+                      tensor_offsets, tensor_tiles);
+        return DF11_OK;
+    } catch (...) {
+        return DF11_E_INVALID;
+    }
 }
 
 int df11_build_codebook(const uint16_t *const *tensors, const uint64_t *numel, uint32_t n_tensors,
@@ -629,28 +691,18 @@ int df11_encode_fmt(uint32_t format, const df11_codebook *cb, const void *const 
         }
 
         // per-tensor element offsets and tile ranges
-        uint64_t g = 0, bit = 0;
+        std::vector<uint64_t> bits(n_tensors, 0);
+        std::vector<uint32_t> last_sym(n_tensors, 0);
+        for (size_t p = 0; p < pieces.size(); p++) bits[pieces[p].tensor] += start[p + 1] - start[p];
         for (uint32_t k = 0; k < n_tensors; k++) {
-            out->tensor_offsets[k] = g;
-            uint64_t bits_k = 0;
-            for (size_t p = 0; p < pieces.size(); p++)
-                if (pieces[p].tensor == k) bits_k += start[p + 1] - start[p];
-            out->tensor_tiles[2 * k] = bit >> tshift;
-            if (numel[k]) {
-                uint32_t last_sym = 0;
-                with_format(format, [&](auto fm) {
-                    using Fm = decltype(fm);
-                    last_sym = Fm::sym(static_cast<const typename Fm::T *>(tensors[k])[numel[k] - 1]);
-                });
-                const uint64_t last_start = bit + bits_k - cb->code_len[last_sym];
-                out->tensor_tiles[2 * k + 1] = (last_start >> tshift) + 1;
-            } else {
-                out->tensor_tiles[2 * k + 1] = out->tensor_tiles[2 * k];
-            }
-            g += numel[k];
-            bit += bits_k;
+            if (!numel[k]) continue;
+            with_format(format, [&](auto fm) {
+                using Fm = decltype(fm);
+                last_sym[k] = Fm::sym(static_cast<const typename Fm::T *>(tensors[k])[numel[k] - 1]);
+            });
         }
-        out->tensor_offsets[n_tensors] = n;
+        tensor_ranges(cb, numel, bits.data(), last_sym.data(), n_tensors, tshift,
+                      out->tensor_offsets, out->tensor_tiles);
 
         uint32_t mx = 0;
         for (uint64_t t = 0; t < sz.n_tiles; t++)

@@ -256,6 +256,25 @@ int df11_encode_size_from_counts(uint32_t format, const df11_codebook *cb, const
                                  uint64_t n_weights, uint32_t tile_windows, uint32_t window_bytes,
                                  df11_sizes *out);
 
+/*
+ * df11_tensor_ranges_from_counts -- host.  The tensor_offsets and
+ * tensor_tiles arrays that df11_encode writes (see df11_host_stream), from
+ * per-tensor exponent histograms instead of the weights, for a unit encoded
+ * elsewhere (df11_encode_device): counts holds n_tensors rows of 256 uint64,
+ * row k the histogram of tensor k (its sum is the tensor's weight count);
+ * last_weights[k] is the bit pattern of tensor k's last weight (ignored for
+ * an empty tensor), whose symbol's code is the tensor's last.  Writes
+ * tensor_offsets[0 .. n_tensors] and tensor_tiles[0 .. 2 n_tensors).
+ * Errors: DF11_E_INVALID (null pointers, layout, a last weight whose symbol
+ * the row does not count, N >= 2^32), DF11_E_SYMBOL (a counted symbol without
+ * a code).
+ */
+int df11_tensor_ranges_from_counts(uint32_t format, const df11_codebook *cb,
+                                   const uint64_t *counts, const uint32_t *last_weights,
+                                   uint32_t n_tensors, uint32_t tile_windows,
+                                   uint32_t window_bytes, uint64_t *tensor_offsets,
+                                   uint64_t *tensor_tiles);
+
 /* df11_encode for any df11_format (FP8 requires T = 64); out->format is set. */
 int df11_encode_fmt(uint32_t format, const df11_codebook *cb, const void *const *tensors,
                     const uint64_t *numel, uint32_t n_tensors, uint32_t tile_windows,

@@ -95,3 +95,27 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
                          check=True).stdout
     assert out.startswith("1 "), out
+
+
+def test_empty_unit_claiming_tiles_is_rejected_before_any_launch():
+    """A descriptor with no weights but tiles or bits is inconsistent: every
+    device entry point rejects it on the host (its pointers are null, so a
+    launch would read through them)."""
+    import ctypes
+
+    import entropy_decoding_amd as ed
+
+    for n_tiles, total_bits in ((1, 0), (1, 64), (0, 8)):
+        d = ed.df11_device_stream()
+        d.n_weights, d.n_tiles, d.total_bits = 0, n_tiles, total_bits
+        d.tile_windows, d.window_bytes, d.n_luts = 64, 8, 1
+        counts = ctypes.c_void_p(0x1000)  # never dereferenced: the call returns first
+        assert ed.LIB.df11_window_counts(ctypes.byref(d), counts, None) == ed.DF11_E_INVALID
+        assert ed.LIB.df11_decompress_block(ctypes.byref(d), counts, None, None) == ed.DF11_E_INVALID
+    # more weights than bits, or more bits than 32 per weight, cannot be a valid unit
+    for n, bits in ((100, 99), (2, 65)):
+        d = ed.df11_device_stream()
+        d.n_weights, d.total_bits, d.n_tiles = n, bits, 1
+        d.tile_windows, d.window_bytes, d.n_luts = 64, 8, 1
+        assert ed.LIB.df11_decompress_block(ctypes.byref(d), ctypes.c_void_p(0x1000), None,
+                                            None) == ed.DF11_E_INVALID

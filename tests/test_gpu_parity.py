@@ -243,6 +243,69 @@ def test_phase1_window_counts_8b_block_full_size():
     check_window_counts(u, oracle.exponents(_cat(tensors)), "cfg1 block")
 
 
+def _corrupt_level_tables(u):
+    """Replace the unit's device tables by an image whose hierarchical tables
+    1.. hold only pointers back to table 1, so that no code longer than the
+    fast tables' index reaches a leaf."""
+    bad = ed.df11_codebook.from_buffer_copy(u.cb)
+    for k in range(1, int(bad.n_luts)):
+        for b in range(256):
+            bad.lut[k][b] = 0x8001
+    u.ds.tables.copy_(torch.from_numpy(ed.table_image(bad)))
+
+
+def test_phase1_flags_windows_whose_codes_reach_no_leaf(unit_tensors):
+    """A code that the tables cannot resolve adds 2^20 to its window's count:
+    exactly the windows where a code longer than the 12-bit count table starts
+    are flagged, the others keep the oracle's counts, and a flagged window's
+    low bits count the codes before its first long one."""
+    (w,) = unit_tensors("0")
+    u = Unit([w])
+    assert u.cb.n_luts > 1 and u.cb.max_len > ed.DF11_COUNT_BITS
+    _corrupt_level_tables(u)
+    n = int(u.hs.n_tiles) * u.tw
+    c = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    say(f"[gpu] df11_window_counts with unresolvable long codes windows={n}")
+    ed.df11_window_counts(u.ds, c)
+    torch.cuda.synchronize()
+    got = c.cpu().numpy().view(np.uint32)
+    sym = oracle.exponents(w)
+    lens = oracle.code_lengths(oracle.histogram_symbols(sym))
+    ln = lens[sym].astype(np.int64)
+    win = (np.cumsum(ln) - ln) // 64  # window of every code start
+    ref = np.bincount(win, minlength=n).astype(np.uint32)
+    longw = np.unique(win[ln > ed.DF11_COUNT_BITS])
+    flagged = np.flatnonzero(got >= (1 << 20))
+    assert longw.size > 0 and np.array_equal(flagged, longw)
+    ok = np.setdiff1d(np.arange(n), longw)
+    assert np.array_equal(got[ok], ref[ok])
+    first_code = np.searchsorted(win, longw)
+    first_long = np.array([int(np.flatnonzero((win == j) & (ln > ed.DF11_COUNT_BITS))[0]) for j in longw])
+    assert np.array_equal(got[longw] - (1 << 20), first_long - first_code)
+
+
+def test_unresolvable_codes_are_reported_by_the_decoder(unit_tensors):
+    """The same tables in a decompression: the flagged tiles fail their count
+    check (DF11_E_CORRUPT) and write nothing; tiles without codes longer than
+    the 10-bit multi-symbol index never use those tables and stay exact."""
+    (w,) = unit_tensors("0")
+    u = Unit([w])
+    _corrupt_level_tables(u)
+    out, st = u.decompress(-1, "unresolvable long codes")
+    assert st == ed.DF11_E_CORRUPT
+    got = out.cpu().numpy().view(np.uint16)
+    sym = oracle.exponents(w)
+    lens = oracle.code_lengths(oracle.histogram_symbols(sym))
+    ln = lens[sym].astype(np.int64)
+    tile = (np.cumsum(ln) - ln) // (64 * u.tw)
+    bop = u.hs.block_out_pos.astype(np.int64)
+    long_tiles = set(np.unique(tile[ln > ed.DF11_MULTI_BITS]).tolist())
+    clean = [t for t in range(int(u.hs.n_tiles)) if t not in long_tiles]
+    assert len(clean) > 0
+    for t in clean:  # a tile writes only its own outputs [bop[t], bop[t+1])
+        assert np.array_equal(got[bop[t]:bop[t + 1]], w[bop[t]:bop[t + 1]]), t
+
+
 # ------------------------------------------------------------------ failure paths
 
 

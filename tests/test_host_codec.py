@@ -384,3 +384,73 @@ def test_random_units_match_oracle_property():
         _compare(tensors, data.draw(st.sampled_from([64, 256, 512]), label="tile windows"), 8)
 
     check()
+
+
+# ------------------------------------------------- tensor ranges from histograms
+
+
+def _oracle_ranges(tensors, lens, tile_bits, fmt):
+    """Element offsets and tile ranges from the oracle's code start bits."""
+    offs = [0]
+    tiles = []
+    bit = 0
+    for t in tensors:
+        t = np.asarray(t).reshape(-1)
+        if fmt == "bf16":
+            sym = oracle.exponents(t)
+        else:
+            sym = oracle.fp8_split(t, fmt.split("_")[1])[0]
+        ln = lens[sym].astype(np.int64)
+        if t.size:
+            last_start = bit + int(ln.sum()) - int(ln[-1])
+            tiles += [bit // tile_bits, last_start // tile_bits + 1]
+        else:
+            tiles += [bit // tile_bits, bit // tile_bits]
+        bit += int(ln.sum())
+        offs.append(offs[-1] + t.size)
+    return offs, tiles
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tensor_ranges_from_counts_match_the_oracle(seed):
+    rng = np.random.default_rng(700 + seed)
+    fmt = ["bf16", "bf16", "fp8_e4m3", "bf16", "fp8_e5m2", "bf16"][seed]
+    tw = 64 if fmt != "bf16" else int(rng.choice([64, 256, 512]))
+    tensors = []
+    for _ in range(int(rng.integers(1, 7))):
+        n = int(rng.choice([0, 1, 7, 4095, 4096, int(rng.integers(1, 90_000))]))
+        w = ((rng.standard_normal(n).astype(np.float32) * float(rng.choice([0.02, 3.0])))
+             .view(np.uint32) >> 16).astype(np.uint16)
+        tensors.append(w if fmt == "bf16" else _fp8(w, fmt.split("_")[1]))
+    if not any(np.asarray(t).size for t in tensors):  # a codebook needs one weight
+        tensors.append(np.full(3, 0x3C00, np.uint16) if fmt == "bf16" else np.full(3, 0x38, np.uint8))
+    cb = ed.df11_build_codebook(tensors, fmt)
+    hs = ed.df11_encode(cb, tensors, tw, 8, fmt)
+    if fmt == "bf16":
+        counts = [oracle.histogram(t) for t in tensors]
+    else:
+        counts = [oracle.histogram_symbols(oracle.fp8_split(t, fmt.split("_")[1])[0]) for t in tensors]
+    last = [int(np.asarray(t).reshape(-1)[-1]) if np.asarray(t).size else 0 for t in tensors]
+    offs, tiles = ed.df11_tensor_ranges_from_counts(cb, np.array(counts), last, fmt, tw, 8)
+    lens = ed.codebook_arrays(cb)[0]
+    o_offs, o_tiles = _oracle_ranges(tensors, lens, 64 * tw, fmt)
+    assert offs.tolist() == o_offs and tiles.tolist() == o_tiles
+    assert np.array_equal(offs, hs.tensor_offsets) and np.array_equal(tiles, hs.tensor_tiles)
+
+
+def test_tensor_ranges_from_counts_errors():
+    w = np.arange(0x3C00, 0x3C40, dtype=np.uint16)
+    cb = ed.df11_build_codebook([w])
+    c = oracle.histogram(w)
+    with pytest.raises(ed.Df11Error) as e:  # the last weight's symbol is not counted
+        ed.df11_tensor_ranges_from_counts(cb, c[None, :], [0x7F80])
+    assert e.value.status == ed.DF11_E_INVALID
+    bad = c.copy()
+    bad[200] = 5  # a symbol without a code
+    with pytest.raises(ed.Df11Error) as e:
+        ed.df11_tensor_ranges_from_counts(cb, bad[None, :], [int(w[-1])])
+    assert e.value.status == ed.DF11_E_SYMBOL
+    with pytest.raises(ed.Df11Error):
+        ed.df11_tensor_ranges_from_counts(cb, c[None, :], [int(w[-1])], "bf16", 100, 8)
+    offs, tiles = ed.df11_tensor_ranges_from_counts(cb, np.zeros((0, 256), np.uint64), [])
+    assert offs.tolist() == [0] and tiles.size == 0

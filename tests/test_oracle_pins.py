@@ -328,6 +328,24 @@ def test_aux_arrays_drive_an_independent_window_decoder(threads, bpt):
     assert bop[-1] == w.size
 
 
+@pytest.mark.parametrize("alphabet,threads,bpt", [(16, 4, 8), (32, 8, 8), (16, 3, 16)])
+def test_fp8_aux_arrays_drive_an_independent_window_decoder(alphabet, threads, bpt):
+    """The FP8 symbol-sequence encoder's aux arrays (E4M3: 16 exponent values,
+    E5M2: 32) consumed by the same independent window decoder as the BF16 ones."""
+    rng = np.random.default_rng(alphabet * 10 + threads)
+    p = np.r_[[0.32, 0.24, 0.16, 0.1], np.full(alphabet - 4, 0.18 / (alphabet - 4))]
+    sym = rng.choice(alphabet, size=6000, p=p).astype(np.uint8)
+    sym[::131] = alphabet - 1  # rare values take the longest codes
+    cb = oracle.codebook_symbols(sym)
+    stream, total = oracle.encode_symbols(sym, cb)
+    gaps, bop = oracle.aux_symbols(sym, cb, threads, bpt)
+    padded = np.zeros(gaps.size * bpt + 8, dtype=np.uint8)
+    padded[: stream.size] = stream
+    syms = _py_decode_windows(padded, total, cb.lens, cb.codes, gaps, bop, threads, bpt)
+    assert syms == sym.tolist()
+    assert bop[-1] == sym.size
+
+
 # ------------------------------------------------------------ the pages' numbers
 
 
