@@ -188,6 +188,9 @@ def _load():
     L.df11_decompress_gemv.argtypes = [ctypes.POINTER(df11_device_stream),
                                        ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32, vp, vp,
                                        vp, ctypes.c_uint64, vp, vp]
+    L.df11_decompress_gemv_noalloc.argtypes = [ctypes.POINTER(df11_device_stream),
+                                               ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32,
+                                               vp, vp, vp, vp]
     L.df11_gemm_order.argtypes = [_u16p, ctypes.c_uint32, ctypes.c_uint32, _u16p]
     L.df11_decompress_gemm_scratch_bytes.argtypes = [ctypes.POINTER(df11_gemv_tensor),
                                                      ctypes.c_uint32, ctypes.c_uint32]
@@ -215,7 +218,8 @@ def _load():
               L.df11_pipeline_release, L.df11_gemv_bf16, L.df11_build_codebook_from_counts,
               L.df11_encode_size_from_counts, L.df11_histogram_device, L.df11_encode_device,
               L.df11_decompress_gemv, L.df11_gemm_order, L.df11_decompress_gemm,
-              L.df11_window_counts, L.df11_tensor_ranges_from_counts):
+              L.df11_window_counts, L.df11_tensor_ranges_from_counts,
+              L.df11_decompress_gemv_noalloc):
         f.restype = ctypes.c_int
     return L
 
@@ -726,6 +730,25 @@ def df11_decompress_gemv(ds: DeviceStream, layout, x, y, scratch=None, status=No
                                     ctypes.c_void_p(y.data_ptr()),
                                     ctypes.c_void_p(scratch.data_ptr()), scratch.numel(), sp,
                                     _stream_handle(stream)))
+
+
+DF11_GEMV_NOALLOC_MAX_TILES = 786432
+
+
+def df11_decompress_gemv_noalloc(ds: DeviceStream, layout, x, y, status=None,
+                                 stream=None) -> None:
+    """df11_decompress_gemv on the library's static per-GPU workspace (no
+    allocation anywhere in the call; units of at most
+    DF11_GEMV_NOALLOC_MAX_TILES tiles; calls on one GPU must not overlap)."""
+    arr, n, nx, ny = layout
+    if x.dtype.itemsize != 4 or y.dtype.itemsize != 4 or x.numel() < nx or y.numel() < ny:
+        raise ValueError("x and y must be float32 device tensors covering the layout")
+    sp = ctypes.c_void_p(status.data_ptr()) if status is not None else ctypes.c_void_p(0)
+    _check("df11_decompress_gemv_noalloc",
+           LIB.df11_decompress_gemv_noalloc(ctypes.byref(ds.desc), arr, n,
+                                            ctypes.c_void_p(x.data_ptr()),
+                                            ctypes.c_void_p(y.data_ptr()), sp,
+                                            _stream_handle(stream)))
 
 
 def table_bytes(cb: df11_codebook) -> int:

@@ -54,6 +54,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "df11.h"
 #include "df11_launch.h"
@@ -1567,9 +1568,15 @@ uint64_t df11_decompress_gemv_scratch_bytes(const df11_device_stream *s) {
     return s ? s->n_tiles * (4u * kRowsPerTile + 4u) + 256u : 0u;
 }
 
-int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t, uint32_t n_tensors,
-                         const float *x, float *y, void *scratch, uint64_t scratch_bytes,
-                         int32_t *d_status, df11_hip_stream st) {
+}  // extern "C"
+
+namespace {
+
+// df11_decompress_gemv on a given workspace (the caller's, or the library's
+// static one for df11_decompress_gemv_noalloc)
+int gemv_impl(const df11_device_stream *s, const df11_gemv_tensor *t, uint32_t n_tensors,
+              const float *x, float *y, void *scratch, uint64_t scratch_bytes, int32_t *d_status,
+              df11_hip_stream st) {
     KArgs a{};
     int rc = prepare(s, a);
     if (rc != DF11_OK) return rc;
@@ -1640,6 +1647,67 @@ int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t,
                : DF11_E_HIP;
 }
 
+// The workspace of df11_decompress_gemv_noalloc: per-tile row sums and first
+// rows for up to DF11_GEMV_NOALLOC_MAX_TILES tiles.  In host code `scratch`
+// names a host-side stand-in; kernels get its device address, looked up once
+// per device.
+constexpr uint64_t kNoAllocScratchBytes =
+    uint64_t(DF11_GEMV_NOALLOC_MAX_TILES) * (4u * kRowsPerTile + 4u) + 256u;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once known
+
+// The device address of `scratch` on the current device.  The first call on
+// a device asks the runtime for it (with that device current); later calls
+// reuse it.  No memory is allocated: the array is part of the loaded code
+// object on every device.
+int scratch_on_current_device(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DF11_E_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return DF11_E_INVALID;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DF11_E_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DF11_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *t, uint32_t n_tensors,
+                         const float *x, float *y, void *scratch_buf, uint64_t scratch_bytes,
+                         int32_t *d_status, df11_hip_stream st) {
+    return gemv_impl(s, t, n_tensors, x, y, scratch_buf, scratch_bytes, d_status, st);
+}
+
+int df11_decompress_gemv_noalloc(const df11_device_stream *s, const df11_gemv_tensor *t,
+                                 uint32_t n_tensors, const float *x, float *y, int32_t *d_status,
+                                 df11_hip_stream st) {
+    if (s && s->n_tiles > DF11_GEMV_NOALLOC_MAX_TILES) return DF11_E_CAPACITY;
+    if (s && s->n_weights && df11_decompress_gemv_scratch_bytes(s) > kNoAllocScratchBytes)
+        return DF11_E_CAPACITY;
+    // argument errors first, so that a rejected call touches no device state
+    KArgs probe{};
+    const int rc = prepare(s, probe);
+    if (rc != DF11_OK) return rc;
+    void *ws = nullptr;
+    const int r2 = scratch_on_current_device(&ws);
+    if (r2 != DF11_OK) return r2;
+    return gemv_impl(s, t, n_tensors, x, y, ws, kNoAllocScratchBytes, d_status, st);
+}
+
 }  // extern "C"
 
 namespace {
@@ -1670,16 +1738,16 @@ uint64_t df11_decompress_gemm_scratch_bytes(const df11_gemv_tensor *t, uint32_t 
 }
 
 int df11_decompress_gemm(const df11_device_stream *s, const df11_gemv_tensor *t, uint32_t n_tensors,
-                         uint32_t n_tokens, const uint16_t *x, float *y, void *scratch,
-                         uint64_t scratch_bytes, int32_t *d_status, df11_hip_stream st) {
+                         uint32_t n_tokens, const uint16_t *x, float *y, void *work,
+                         uint64_t work_bytes, int32_t *d_status, df11_hip_stream st) {
     KArgs a{};
     int rc = prepare(s, a);
     if (rc != DF11_OK) return rc;
     const uint32_t nb = n_tokens / 16;
     if (s->format != DF11_FORMAT_BF16 || s->tile_windows != 64 || s->n_weights == 0 || !t ||
         n_tensors == 0 || n_tensors > DF11_GEMV_MAX_TENSORS || n_tokens % 16 || nb < 1 || nb > 4 ||
-        !x || !y || !scratch || !aligned(x, 16) || !aligned(y, 16) || !aligned(scratch, 16) ||
-        scratch_bytes < df11_decompress_gemm_scratch_bytes(t, n_tensors, n_tokens))
+        !x || !y || !work || !aligned(x, 16) || !aligned(y, 16) || !aligned(work, 16) ||
+        work_bytes < df11_decompress_gemm_scratch_bytes(t, n_tensors, n_tokens))
         return DF11_E_INVALID;
     // longest segments first: their workgroups take the longest
     uint32_t order[DF11_GEMV_MAX_TENSORS], sbl[DF11_GEMV_MAX_TENSORS], seg[DF11_GEMV_MAX_TENSORS];
@@ -1743,13 +1811,13 @@ int df11_decompress_gemm(const df11_device_stream *s, const df11_gemv_tensor *t,
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
         return DF11_E_INVALID;
     hipStream_t hs = static_cast<hipStream_t>(st);
-    uint16_t *xs = static_cast<uint16_t *>(scratch);
+    uint16_t *xs = static_cast<uint16_t *>(work);
     if (df11_detail::launch(df11_gemm_x_order, dim3(uint32_t((chunks + kThreads - 1) / kThreads)),
                             dim3(kThreads), 0, hs, g, n_tokens, x, xs) != hipSuccess)
         return DF11_E_HIP;
     const uint32_t grid = uint32_t((mbs + kXcdBlock - 1) / kXcdBlock * kXcdBlock);
     const uint16_t *xsp = xs;
-    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(scratch) +
+    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(work) +
                                             (2 * chunks * 8 + 15) / 16 * 16);
     void *args[] = {&a, &g, &xsp, &y, &part};
     if (hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, lds, hs) != hipSuccess)

@@ -37,7 +37,9 @@
  *
  * Conventions.  Every call returns a df11_status.  No call allocates device
  * memory, frees caller memory or synchronises a stream; host calls may use
- * worker threads internally and are thread-safe (no global mutable state).
+ * worker threads internally and are thread-safe.  The only global state is
+ * the per-device address of df11_decompress_gemv_noalloc's static workspace,
+ * set once under a lock.
  */
 #ifndef DF11_H
 #define DF11_H
@@ -462,6 +464,29 @@ uint64_t df11_decompress_gemv_scratch_bytes(const df11_device_stream *s);
 int df11_decompress_gemv(const df11_device_stream *s, const df11_gemv_tensor *tensors,
                          uint32_t n_tensors, const float *x, float *y, void *scratch,
                          uint64_t scratch_bytes, int32_t *d_status, df11_hip_stream st);
+
+/*
+ * df11_decompress_gemv_noalloc -- device.  For callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): df11_decompress_gemv with the library's own
+ * workspace instead of a caller's.  That workspace is one static device array
+ * per GPU of DF11_GEMV_NOALLOC_MAX_TILES * 20 + 256 bytes (15 MiB), held from
+ * the library's load until the process ends; the call itself allocates
+ * nothing.  Same arguments (minus the workspace), products, summation order
+ * and errors as df11_decompress_gemv, plus DF11_E_CAPACITY, returned before
+ * anything is launched, for a unit of more than DF11_GEMV_NOALLOC_MAX_TILES
+ * tiles (a Llama-3-70B-shaped block has about 558,000).  Every call on a GPU
+ * shares that GPU's workspace: calls that may overlap on one GPU (different
+ * streams, or different host threads) race and must be ordered by the
+ * caller.  Nothing in the workspace needs clearing between calls (every tile
+ * of a valid unit writes its entries before the second launch reads them).
+ * The first call on a device looks the workspace's address up on that
+ * device (it must be the current device) and keeps it.
+ */
+#define DF11_GEMV_NOALLOC_MAX_TILES 786432u
+int df11_decompress_gemv_noalloc(const df11_device_stream *s, const df11_gemv_tensor *tensors,
+                                 uint32_t n_tensors, const float *x, float *y,
+                                 int32_t *d_status, df11_hip_stream st);
 
 /*
  * df11_gemm_order -- host, the weight order that df11_decompress_gemm reads:
