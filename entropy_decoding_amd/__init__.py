@@ -181,6 +181,7 @@ def _load():
                                            vp, vp]
     L.df11_pipeline_acquire.argtypes = [vp, ctypes.c_uint32, vp]
     L.df11_pipeline_release.argtypes = [vp, ctypes.c_uint32, vp]
+    L.df11_pipeline_set_decode_share.argtypes = [vp, ctypes.c_uint32]
     L.df11_gemv_bf16.argtypes = [vp, ctypes.POINTER(df11_gemv_tensor), ctypes.c_uint32, vp, vp, vp]
     L.df11_build_codebook_from_counts.argtypes = [_u64p, ctypes.POINTER(df11_codebook)]
     L.df11_decompress_gemv_scratch_bytes.argtypes = [ctypes.POINTER(df11_device_stream)]
@@ -215,7 +216,8 @@ def _load():
               L.df11_build_codebook_fmt, L.df11_encode_size_fmt, L.df11_encode_fmt,
               L.df11_decompress_block, L.df11_decompress_tensor, L.df11_pipeline_create,
               L.df11_pipeline_destroy, L.df11_pipeline_decompress, L.df11_pipeline_acquire,
-              L.df11_pipeline_release, L.df11_gemv_bf16, L.df11_build_codebook_from_counts,
+              L.df11_pipeline_release, L.df11_pipeline_set_decode_share, L.df11_gemv_bf16,
+              L.df11_build_codebook_from_counts,
               L.df11_encode_size_from_counts, L.df11_histogram_device, L.df11_encode_device,
               L.df11_decompress_gemv, L.df11_gemm_order, L.df11_decompress_gemm,
               L.df11_window_counts, L.df11_tensor_ranges_from_counts,
@@ -488,6 +490,11 @@ class Pipeline:
         _check("df11_pipeline_decompress",
                LIB.df11_pipeline_decompress(self._p, int(slot), ctypes.byref(ds.desc),
                                             ctypes.c_void_p(out.data_ptr()), sp))
+
+    def set_decode_share(self, workgroups_per_cu: int) -> None:
+        """Cap the decode at this many workgroups per compute unit (0: full grid)."""
+        _check("df11_pipeline_set_decode_share",
+               LIB.df11_pipeline_set_decode_share(self._p, int(workgroups_per_cu)))
 
     def acquire(self, slot: int, consumer_stream) -> None:
         _check("df11_pipeline_acquire",

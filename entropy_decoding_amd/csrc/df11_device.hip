@@ -1476,7 +1476,8 @@ int prepare(const df11_device_stream *s, KArgs &a) {
     return DF11_OK;
 }
 
-int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t st) {
+int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t st,
+           uint32_t cap_per_cu = 0) {
     if (n_tiles == 0) return DF11_OK;
     a.n_tiles = n_tiles;
     // one staging buffer per workgroup, or one per wave for 64-window tiles
@@ -1495,7 +1496,8 @@ int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t 
     const uint64_t resident = uint64_t(cus) * per_cu;
     const uint64_t slots = (uint64_t(n_tiles) + per_wg - 1) / per_wg;  // workgroups with a tile
     const uint64_t per = s->format == DF11_FORMAT_BF16 ? kTilesPerWorkgroup : kTilesPerWorkgroupFp8;
-    const uint64_t want = std::max<uint64_t>(resident, (slots + per - 1) / per);
+    uint64_t want = std::max<uint64_t>(resident, (slots + per - 1) / per);
+    if (cap_per_cu) want = std::min<uint64_t>(want, uint64_t(cus) * std::min<uint32_t>(cap_per_cu, per_cu));
     const uint64_t used = std::min<uint64_t>(slots, want);
     const uint32_t grid = uint32_t((used + kXcdBlock - 1) / kXcdBlock * kXcdBlock);
     void *args[] = {&a};
@@ -1505,10 +1507,9 @@ int launch(const df11_device_stream *s, KArgs &a, uint32_t n_tiles, hipStream_t 
 
 }  // namespace
 
-extern "C" {
-
-int df11_decompress_block(const df11_device_stream *s, void *out, int32_t *d_status,
-                          df11_hip_stream st) {
+int df11_detail::decompress_block_capped(const df11_device_stream *s, void *out,
+                                         int32_t *d_status, hipStream_t st,
+                                         uint32_t workgroups_per_cu) {
     KArgs a{};
     int rc = prepare(s, a);
     if (rc != DF11_OK || s->n_weights == 0) return rc;
@@ -1519,7 +1520,14 @@ int df11_decompress_block(const df11_device_stream *s, void *out, int32_t *d_sta
     a.out_lo = 0;
     a.out_hi = uint32_t(s->n_weights);
     a.out_shift = 0;
-    return launch(s, a, uint32_t(s->n_tiles), static_cast<hipStream_t>(st));
+    return launch(s, a, uint32_t(s->n_tiles), st, workgroups_per_cu);
+}
+
+extern "C" {
+
+int df11_decompress_block(const df11_device_stream *s, void *out, int32_t *d_status,
+                          df11_hip_stream st) {
+    return df11_detail::decompress_block_capped(s, out, d_status, static_cast<hipStream_t>(st), 0);
 }
 
 int df11_window_counts(const df11_device_stream *s, uint32_t *counts, df11_hip_stream st) {

@@ -8,6 +8,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "df11.h"
+
 #include <cstddef>
 #include <tuple>
 #include <utility>
@@ -28,5 +30,13 @@ hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_
     std::tuple<P...> t(std::forward<A>(args)...);
     return launch_tuple(k, grid, block, lds, st, t, std::index_sequence_for<P...>{});
 }
+
+// df11_decompress_block with the grid capped at workgroups_per_cu resident
+// workgroups per compute unit (0: the default grid).  Each wave loops over
+// the tiles with the grid's stride, so any grid decodes every tile; a capped
+// grid leaves the other workgroup slots of every compute unit to kernels on
+// other streams.
+int decompress_block_capped(const df11_device_stream *s, void *out, int32_t *d_status,
+                            hipStream_t st, uint32_t workgroups_per_cu);
 
 }  // namespace df11_detail

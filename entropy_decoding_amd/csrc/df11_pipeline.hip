@@ -12,6 +12,7 @@
 #include <new>
 
 #include "df11.h"
+#include "df11_launch.h"
 
 struct df11_pipeline {
     hipStream_t decode;
@@ -20,6 +21,7 @@ struct df11_pipeline {
     hipEvent_t released[DF11_PIPELINE_MAX_SLOTS];  // the consumer has finished reading it
     bool filled[DF11_PIPELINE_MAX_SLOTS];
     bool was_released[DF11_PIPELINE_MAX_SLOTS];
+    uint32_t decode_share;  // workgroups per compute unit for the decode (0: full grid)
 };
 
 namespace {
@@ -203,10 +205,17 @@ int df11_pipeline_decompress(df11_pipeline *p, uint32_t slot, const df11_device_
     // the slot's previous contents must have been released by their consumer
     if (p->was_released[slot] && hipStreamWaitEvent(p->decode, p->released[slot], 0) != hipSuccess)
         return DF11_E_HIP;
-    const int rc = df11_decompress_block(s, out, d_status, p->decode);
+    const int rc = df11_detail::decompress_block_capped(s, out, d_status, p->decode,
+                                                        p->decode_share);
     if (rc != DF11_OK) return rc;
     if (hipEventRecord(p->ready[slot], p->decode) != hipSuccess) return DF11_E_HIP;
     p->filled[slot] = true;
+    return DF11_OK;
+}
+
+int df11_pipeline_set_decode_share(df11_pipeline *p, uint32_t workgroups_per_cu) {
+    if (!p || workgroups_per_cu > 64) return DF11_E_INVALID;
+    p->decode_share = workgroups_per_cu;
     return DF11_OK;
 }
 

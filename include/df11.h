@@ -410,6 +410,16 @@ int df11_pipeline_destroy(df11_pipeline *p);
 int df11_pipeline_decompress(df11_pipeline *p, uint32_t slot, const df11_device_stream *s,
                              void *out, int32_t *d_status);
 
+/* How much of the GPU the pipeline's decompressions take: at most
+ * workgroups_per_cu resident workgroups per compute unit (a persistent grid
+ * of that many workgroups per compute unit of the device, whose waves loop
+ * over the tiles), leaving the rest of every compute unit
+ * to the consumer's kernels, which then run beside the decode instead of
+ * waiting for its workgroups to drain.  0 (the default) launches the full
+ * grid of df11_decompress_block.  Applies to later df11_pipeline_decompress
+ * calls.  DF11_E_INVALID for a null pipeline or a value above 64. */
+int df11_pipeline_set_decode_share(df11_pipeline *p, uint32_t workgroups_per_cu);
+
 /* Makes the consumer stream wait until the slot's latest decompression is
  * done.  DF11_E_INVALID if the slot was never filled. */
 int df11_pipeline_acquire(df11_pipeline *p, uint32_t slot, df11_hip_stream consumer);

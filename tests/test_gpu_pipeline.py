@@ -117,8 +117,9 @@ def _blocks(seed, n_blocks):
     return blocks
 
 
-@pytest.mark.parametrize("n_slots", [2, 3])
-def test_pipelined_results_equal_sequential_results(n_slots):
+@pytest.mark.parametrize("n_slots,share", [(2, 0), (3, 0), (2, 1), (3, 2)])
+def test_pipelined_results_equal_sequential_results(n_slots, share):
+    """(share: the decode's workgroups per compute unit; 0 is the full grid)"""
     blocks = _blocks(100 + n_slots, 7)
     nmax = max(ds.n_weights for _, _, ds in blocks)
     bufs = [torch.empty(nmax, dtype=torch.int16, device="cuda") for _ in range(n_slots)]
@@ -132,7 +133,8 @@ def test_pipelined_results_equal_sequential_results(n_slots):
 
     decode, compute = torch.cuda.Stream(), torch.cuda.Stream()
     p = ed.Pipeline(decode, n_slots)
-    say(f"[gpu] pipeline n_slots={n_slots} blocks={len(blocks)}")
+    p.set_decode_share(share)
+    say(f"[gpu] pipeline n_slots={n_slots} share={share} blocks={len(blocks)}")
     for i in range(min(n_slots - 1, len(blocks))):
         p.decompress(i % n_slots, blocks[i][2], bufs[i % n_slots], status)
     for i in range(len(blocks)):
@@ -173,5 +175,7 @@ def test_pipeline_argument_errors():
         p.release(1, s)
     with pytest.raises(ed.Df11Error):
         p.acquire(2, s)  # no such slot
+    with pytest.raises(ed.Df11Error):
+        p.set_decode_share(65)  # more workgroups per compute unit than can be resident
     p.close()
     p.close()  # idempotent
