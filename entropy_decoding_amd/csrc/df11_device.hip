@@ -826,9 +826,15 @@ struct BufStoreEpi {
         const uint32_t i = A0 + CH * c + k;
         const bool whole = int32_t(c) >= c_lo && int32_t(c) < c_hi;
         const uint32_t v = F::value1(lane < CH ? sh : sl, k, ebuf[CH * c + k]);
+        // the range is wave-uniform; built from scalars, so that the compiler
+        // does not loop over lanes to find distinct descriptors
+        const uint64_t pe = reinterpret_cast<uint64_t>(static_cast<char *>(a.out) +
+                                                       (int64_t(lo) - int64_t(a.out_shift)) * ES);
+        const uint32_t pe_lo = __builtin_amdgcn_readfirstlane(uint32_t(pe));
+        const uint32_t pe_hi = __builtin_amdgcn_readfirstlane(uint32_t(pe >> 32));
         const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
-            static_cast<char *>(a.out) + (int64_t(lo) - int64_t(a.out_shift)) * ES, 0,
-            any ? (hi - lo) * ES : 0u, 0x00020000);
+            reinterpret_cast<char *>((uint64_t(pe_hi) << 32) | pe_lo), 0,
+            __builtin_amdgcn_readfirstlane(any ? (hi - lo) * ES : 0u), 0x00020000);
         const bool mine = lane < 2 * CH && !whole && i >= lo;
         F::buffer_store1(re, mine ? (i - lo) * ES : kDrop, v);
     }

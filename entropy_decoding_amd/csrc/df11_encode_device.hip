@@ -16,7 +16,12 @@
 //      neighbour (its first or last word, when the group boundary falls
 //      inside a word) into a side array; each code start that is the first
 //      in its window writes the window's gap, and each code start that is
-//      the first in its tile writes that tile's output position;
+//      the first in its tile writes that tile's output position.  A thread
+//      shifts each half of its 16 codes into a 64-bit register pair (with a
+//      second pair marking where each code starts), ORs the half into LDS as
+//      three words, and finds the window and tile starts in its half from
+//      the marks; halves longer than 64 bits, partial groups and codebooks
+//      with codes over 27 bits take the codes one at a time;
 //   4. one thread per group boundary inside a word ORs the two shares and
 //      writes that word (device-wide atomic ORs on the shared words instead
 //      made the encode 35% slower), and the largest tile symbol count.
@@ -89,6 +94,40 @@ __device__ __forceinline__ uint32_t load16(const void *w, uint64_t n, uint64_t i
     }
     return valid;
 }
+
+// The thread's 16 elements as loaded, packed (8 words for BF16, 4 for FP8;
+// zero past n), and their count; element k is field k of the words.
+template <int FMT>
+struct Packed16 {
+    using T = typename Fields<FMT>::T;
+    static constexpr int kWords = sizeof(T) * 4;
+    uint32_t w[kWords];
+    __device__ __forceinline__ uint32_t load(const void *src, uint64_t n, uint64_t i0) {
+        const T *p = static_cast<const T *>(src) + i0;
+        const uint32_t valid = i0 >= n ? 0u : uint32_t(min<uint64_t>(16, n - i0));
+        if (valid == 16) {
+#pragma unroll
+            for (int q = 0; q < kWords / 4; q++) {
+                const uint4 v = reinterpret_cast<const uint4 *>(p)[q];
+                w[4 * q] = v.x;
+                w[4 * q + 1] = v.y;
+                w[4 * q + 2] = v.z;
+                w[4 * q + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kWords; q++) w[q] = 0;
+#pragma unroll
+            for (int k = 0; k < 16; k++)
+                if (uint32_t(k) < valid) w[k * sizeof(T) / 4] |= uint32_t(p[k]) << (8 * sizeof(T) * (k % (4 / sizeof(T))));
+        }
+        return valid;
+    }
+    __device__ __forceinline__ uint32_t elem(int k) const {
+        constexpr int per = 4 / sizeof(T), bits = 8 * sizeof(T);
+        return (w[k / per] >> (bits * (k % per))) & ((1u << bits) - 1u);
+    }
+};
 
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
@@ -240,30 +279,110 @@ struct EmitArgs {
     Codes cb;
 };
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void enc_emit(EmitArgs a) {
+// Codes of at most this length leave the low 5 bits of the code left-aligned
+// in 32 bits zero, so a fast-path table entry can hold the shift 32 - length
+// there: ent = (code << (32 - length)) | (32 - length).
+constexpr uint32_t kPackedMaxLen = 27;
+
+// Bits [j0, j0 + 64) of the bit buffer (MSB first) ORed with the 64-bit
+// string {hi, lo} placed at bit offset r: three words.
+__device__ __forceinline__ void or_string64(uint32_t *buf, uint32_t r, uint32_t hi, uint32_t lo) {
+    const uint32_t s = r & 31u, w = r >> 5;
+    atomicOr(&buf[w], hi >> s);
+    atomicOr(&buf[w + 1], __builtin_amdgcn_alignbit(hi, lo, s));
+    atomicOr(&buf[w + 2], __builtin_amdgcn_alignbit(lo, 0u, s));
+}
+
+// Relative start p (from the half's first bit) of the first code that starts
+// at or after relative position d (0 < d, and some code starts at or after
+// it), from the start marks of a half of B bits (bit j of mark <=> a code
+// starts at relative position B - 1 - j).
+__device__ __forceinline__ uint32_t first_start_at(uint64_t mark, uint32_t B, uint32_t d) {
+    const uint64_t m = mark & ((uint64_t(1) << (B - d)) - 1);  // starts at or after d
+    return B - 1 - (63 - uint32_t(__clzll((long long)m)));
+}
+
+// Held to 80 VGPRs (6 waves per SIMD): uncapped the fast path took 90 and
+// ran slower, and a 64-register cap spilled (70B block: 1.071, 1.041 and
+// 1.006 ms for the encode call uncapped, at 64 and at 80).
+template <int FMT, bool kPacked>
+__global__ __launch_bounds__(kThreads, 6) void enc_emit(EmitArgs a) {
     extern __shared__ uint32_t buf[];  // the workgroup's bits, 32 per word, MSB first
     __shared__ uint32_t wsum[kThreads / 64];
     __shared__ uint32_t code_s[256];
+    __shared__ uint32_t ent_s[256];
     __shared__ uint8_t len_s[256];
     const uint32_t t = threadIdx.x;
     for (uint32_t s = t; s < 256; s += kThreads) {
+        const uint32_t l = a.cb.len[s];
         code_s[s] = a.cb.code[s];
-        len_s[s] = a.cb.len[s];
+        len_s[s] = uint8_t(l);
+        ent_s[s] = (l && l <= kPackedMaxLen) ? (a.cb.code[s] << (32u - l)) | (32u - l) : 0u;
     }
-    uint32_t x[16];
+    Packed16<FMT> xw;
     const uint64_t i0 = uint64_t(blockIdx.x) * kPerGroup + uint64_t(t) * kPerThread;
-    const uint32_t valid = load16<FMT>(a.w, a.n, i0, x);
-    __syncthreads();
-    uint32_t bits = 0;
+    const uint32_t valid = xw.load(a.w, a.n, i0);
+    // sign and mantissa fields (zero past n, like the host encoder's padding),
+    // formed now so that the weights need not stay unpacked
+    uint32_t smw[4];
+    if constexpr (FMT == DF11_FORMAT_BF16) {
 #pragma unroll
-    for (uint32_t k = 0; k < 16; k++) bits += k < valid ? len_s[Fields<FMT>::sym(x[k])] : 0u;
+        for (int q = 0; q < 4; q++) {
+            smw[q] = 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++) smw[q] |= Fields<FMT>::rest(xw.elem(4 * q + k)) << (8 * k);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            smw[q] = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++) smw[q] |= Fields<FMT>::rest(xw.elem(8 * q + k)) << (4 * k);
+        }
+        smw[2] = smw[3] = 0;
+    }
+    __syncthreads();
+
+    // Fast path: each half of 8 codes shifted into {hi, lo} (the string,
+    // right-aligned) and {mh, ml} (a mark at each code's first bit) with
+    // funnel shifts whose shift amount is the entry's own low 5 bits.  A half
+    // fits when all 8 marks survive (it is at most 64 bits long).
+    uint32_t hi[2] = {0, 0}, lo[2] = {0, 0}, mh[2] = {0, 0}, ml[2] = {0, 0};
+    bool fast = kPacked && valid == 16;
+    if (kPacked) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                const uint32_t e = ent_s[Fields<FMT>::sym(xw.elem(8 * h + k))];
+                hi[h] = __builtin_amdgcn_alignbit(hi[h], lo[h], e);
+                lo[h] = __builtin_amdgcn_alignbit(lo[h], e, e);
+                mh[h] = __builtin_amdgcn_alignbit(mh[h], ml[h], e);
+                ml[h] = __builtin_amdgcn_alignbit(ml[h], 0x80000000u, e);
+            }
+            fast = fast && __popc(mh[h]) + __popc(ml[h]) == 8;
+        }
+    }
+    uint32_t B[2] = {0, 0}, last_len[2] = {0, 0};
+    uint32_t bits = 0;
+    if (fast) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const uint64_t mark = (uint64_t(mh[h]) << 32) | ml[h];
+            B[h] = 64u - uint32_t(__clzll((long long)mark));
+            last_len[h] = uint32_t(__ffsll((unsigned long long)mark));  // the last code's mark is at bit length - 1
+        }
+        bits = B[0] + B[1];
+    } else {
+#pragma unroll
+        for (uint32_t k = 0; k < 16; k++) bits += k < valid ? len_s[Fields<FMT>::sym(xw.elem(int(k)))] : 0u;
+    }
     uint32_t total;
     const uint32_t before = block_exclusive(bits, wsum, total);
     const uint64_t g0 = a.start[blockIdx.x];   // first bit of the workgroup
     const uint64_t base = g0 & ~uint64_t(31);  // first bit of buf[0]
     const uint32_t nw = uint32_t((g0 + total - base + 31) >> 5);  // words holding its bits
-    for (uint32_t i = t; i < nw + 1; i += kThreads) buf[i] = 0;
+    for (uint32_t i = t; i < nw + 3; i += kThreads) buf[i] = 0;
     __syncthreads();
 
     // The previous weight's code length decides whether a code is the first
@@ -281,54 +400,72 @@ __global__ __launch_bounds__(kThreads) void enc_emit(EmitArgs a) {
     const uint32_t g0lo = uint32_t(g0), wmask = (1u << a.wshift) - 1, tmask = (1u << a.tshift) - 1;
     uint32_t r = before + (g0lo & 31u);  // start bit of the thread's next code, from base
     uint32_t last = r;                    // start of the thread's last code
+    if (fast) {
 #pragma unroll
-    for (uint32_t k = 0; k < 16; k++) {
-        if (k < valid) {
-            const uint32_t s = Fields<FMT>::sym(x[k]);
-            const uint32_t l = len_s[s], c = code_s[s];
-            const uint32_t pl = (g0lo & ~31u) + r;  // low 32 bits of the absolute start bit
-            if ((pl & wmask) < prev_len) {  // first code start in its window
-                const uint64_t pos = base + r;
-                a.gaps[pos >> a.wshift] = uint8_t(pos & wmask);
+        for (int h = 0; h < 2; h++) {
+            const uint64_t mark = (uint64_t(mh[h]) << 32) | ml[h];
+            // the half's string left-aligned, then ORed in at bit r
+            const uint64_t acc = ((uint64_t(hi[h]) << 32) | lo[h]) << (64u - B[h]);
+            or_string64(buf, r, uint32_t(acc >> 32), uint32_t(acc));
+            const uint32_t pl = (g0lo & ~31u) + r;  // low 32 bits of the half's absolute start
+            const uint32_t span = B[h] - last_len[h];  // relative start of its last code
+            const uint64_t at = base + r;
+            // its first code, after the previous weight's code
+            if ((pl & wmask) < prev_len) a.gaps[at >> a.wshift] = uint8_t(pl & wmask);
+            if ((pl & tmask) < prev_len) a.bop[at >> a.tshift] = uint32_t(i0 + 8 * h);
+            // window and tile boundaries after its first code start, up to its last
+            const uint32_t nwin = ((pl & wmask) + span) >> a.wshift;
+            for (uint32_t i = 1; i <= nwin; i++) {
+                const uint32_t d = (i << a.wshift) - (pl & wmask);
+                const uint32_t p = first_start_at(mark, B[h], d);
+                a.gaps[(at >> a.wshift) + i] = uint8_t(p - d);
             }
-            if ((pl & tmask) < prev_len) {  // first code start in its tile
-                const uint64_t pos = base + r;
-                a.bop[pos >> a.tshift] = uint32_t(i0 + k);
+            const uint32_t ntile = ((pl & tmask) + span) >> a.tshift;
+            for (uint32_t i = 1; i <= ntile; i++) {
+                const uint32_t d = (i << a.tshift) - (pl & tmask);
+                const uint32_t p = first_start_at(mark, B[h], d);
+                // codes of the half that start before p: the marks above p's
+                const uint32_t k = uint32_t(__popcll((unsigned long long)(mark >> (B[h] - p))));
+                a.bop[(at >> a.tshift) + i] = uint32_t(i0 + 8 * h + k);
             }
-            // the code, left-aligned at bit r % 32 of word r / 32, over two words
-            const uint64_t v = uint64_t(c) << (64u - (r & 31u) - l);
-            atomicOr(&buf[r >> 5], uint32_t(v >> 32));
-            atomicOr(&buf[(r >> 5) + 1], uint32_t(v));
-            last = r;
-            prev_len = l;
-            r += l;
+            last = r + span;
+            prev_len = last_len[h];
+            r += B[h];
+        }
+    } else {
+#pragma unroll
+        for (uint32_t k = 0; k < 16; k++) {
+            if (k < valid) {
+                const uint32_t s = Fields<FMT>::sym(xw.elem(int(k)));
+                const uint32_t l = len_s[s], c = code_s[s];
+                const uint32_t pl = (g0lo & ~31u) + r;  // low 32 bits of the absolute start bit
+                if ((pl & wmask) < prev_len) {  // first code start in its window
+                    const uint64_t pos = base + r;
+                    a.gaps[pos >> a.wshift] = uint8_t(pos & wmask);
+                }
+                if ((pl & tmask) < prev_len) {  // first code start in its tile
+                    const uint64_t pos = base + r;
+                    a.bop[pos >> a.tshift] = uint32_t(i0 + k);
+                }
+                // the code, left-aligned at bit r % 32 of word r / 32, over two words
+                const uint64_t v = uint64_t(c) << (64u - (r & 31u) - l);
+                atomicOr(&buf[r >> 5], uint32_t(v >> 32));
+                atomicOr(&buf[(r >> 5) + 1], uint32_t(v));
+                last = r;
+                prev_len = l;
+                r += l;
+            }
         }
     }
     if (valid && i0 + valid == a.n) {  // the last weight: tile boundaries after its start
         for (uint64_t b = ((base + last) >> a.tshift) + 1; b <= a.n_tiles; b++) a.bop[b] = uint32_t(a.n);
     }
-    // sign and mantissa fields (zero past n, like the host encoder's padding);
     // sm_bytes is a multiple of 64, so a thread's 16 or 8 bytes are all inside or all outside
     if ((FMT == DF11_FORMAT_BF16 ? i0 : i0 / 2) < a.sm_bytes) {
-        if constexpr (FMT == DF11_FORMAT_BF16) {
-            uint32_t v[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                v[q] = 0;
-#pragma unroll
-                for (int k = 0; k < 4; k++) v[q] |= (4 * q + k < int(valid) ? Fields<FMT>::rest(x[4 * q + k]) : 0u) << (8 * k);
-            }
-            *reinterpret_cast<uint4 *>(a.sm + i0) = make_uint4(v[0], v[1], v[2], v[3]);
-        } else {
-            uint32_t v[2];
-#pragma unroll
-            for (int q = 0; q < 2; q++) {
-                v[q] = 0;
-#pragma unroll
-                for (int k = 0; k < 8; k++) v[q] |= (8 * q + k < int(valid) ? Fields<FMT>::rest(x[8 * q + k]) : 0u) << (4 * k);
-            }
-            *reinterpret_cast<uint2 *>(a.sm + i0 / 2) = make_uint2(v[0], v[1]);
-        }
+        if constexpr (FMT == DF11_FORMAT_BF16)
+            *reinterpret_cast<uint4 *>(a.sm + i0) = make_uint4(smw[0], smw[1], smw[2], smw[3]);
+        else
+            *reinterpret_cast<uint2 *>(a.sm + i0 / 2) = make_uint2(smw[0], smw[1]);
     }
     __syncthreads();
     // out: words touched only here with plain stores; a word shared with the
@@ -451,13 +588,16 @@ int encode_fmt(const df11_codebook *cb, const void *w, uint64_t n, const df11_si
     a.edge = edge;
     a.wshift = uint32_t(log2u(uint64_t(8) * B));
     a.tshift = a.wshift + uint32_t(log2u(T));
-    a.buf_words = (kPerGroup * DF11_MAX_CODE_LEN + 31) / 32 + 2;
+    a.buf_words = (kPerGroup * DF11_MAX_CODE_LEN + 31) / 32 + 4;
     a.cb = c;
     const size_t lds = size_t(a.buf_words) * 4;
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&enc_emit<FMT>),
+    uint32_t max_len = 0;
+    for (int s = 0; s < 256; s++) max_len = std::max<uint32_t>(max_len, cb->code_len[s]);
+    auto *emit = max_len <= kPackedMaxLen ? enc_emit<FMT, true> : enc_emit<FMT, false>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(emit),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
         return DF11_E_HIP;
-    if (launch(enc_emit<FMT>, dim3(uint32_t(groups)), dim3(kThreads), lds, st, a) != hipSuccess ||
+    if (launch(emit, dim3(uint32_t(groups)), dim3(kThreads), lds, st, a) != hipSuccess ||
         (groups > 1 &&
          launch(enc_edges, dim3(grid_for(groups, kThreads, 1024)), dim3(kThreads), 0, st,
                 static_cast<const uint64_t *>(start), static_cast<const uint32_t *>(edge), groups,
