@@ -111,36 +111,41 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return uint32_t(size_t((const lds8 *)p));
 }
 
-// Hierarchical walk for a code longer than 8 bits at the head of a
-// left-aligned 32-bit window, in lanes where need is set.  The walk starts
-// at level 1: the fast tables hold the index of the level-1 table that the
+// Hierarchical walk for a code longer than the fast tables' index, at the
+// head of a left-aligned 32-bit window, in lanes where need is set.  The
+// walk starts at level 1: the fast entry names the level-1 table that the
 // root would point to, so the root table never needs to be in LDS.
 // lut[(k - 1) * 256 + b] is entry b of table k >= 1; last is the highest
-// table index present (at least 1).  Levels 2 and 3 (codes over 16 bits)
-// run only when some lane needs them.  Returns (length << 8) | symbol, or 0
-// when no leaf is reached by level 3.
+// table index present (at least 1), and table indices are clamped to it so
+// that every read stays inside the tables.  Levels 2 and 3 (codes over 16
+// bits) run only when some lane needs them.  Returns the entry reached: a
+// leaf (bit 15 clear: length << 8 | symbol), or a pointer (bit 15 set) when
+// no leaf is reached by level 3, which a complete code never leaves.
+static_assert(DF11_MAX_LUTS <= 256, "a pointer entry's table index must leave the length field zero");
 __device__ __forceinline__ uint32_t walk_tables(const uint16_t *lut, uint32_t last,
                                                 uint32_t tbl, uint32_t w32, bool need) {
-    const uint32_t k1 = min(max(tbl, 1u), last);
-    uint32_t e = lut[((k1 << 8) | ((w32 >> 16) & 0xFFu)) - 256u];
+    const uint16_t *lm = lut - 256;  // table k at lm + 256 k
+    uint32_t e = lm[(min(tbl, last) << 8) + __builtin_amdgcn_ubfe(w32, 16, 8)];
     if (ballot(need && (e & 0x8000u) != 0)) {
 #pragma unroll
         for (int lvl = 2; lvl < 4; lvl++) {
-            const uint32_t k = min(max(e & 0x7FFFu, 1u), last);
-            const uint32_t next = lut[((k << 8) | ((w32 >> (24 - 8 * lvl)) & 0xFFu)) - 256u];
+            const uint32_t next = lm[(min(e & 0x7FFFu, last) << 8) + __builtin_amdgcn_ubfe(w32, 24 - 8 * lvl, 8)];
             e = (e & 0x8000u) ? next : e;
         }
     }
-    return (e & 0x8000u) ? 0u : (e & 0x3FFFu);
+    return e;
 }
 
-// A multi-symbol entry for a window whose first code is longer than the
-// index; e is the fast-table entry, which holds the level-1 table index.
-__device__ __forceinline__ uint32_t long_entry(const uint16_t *lut, uint32_t last, uint32_t e,
+// A multi-symbol entry (one code) for a window whose first code is longer
+// than the index; t is the fast-table entry, which holds the level-1 table
+// index.  The symbol goes to byte 0 and the length to bits 29..24, with the
+// count 1; a length of 0, or a pointer left by a damaged table, is taken as
+// 1 so that the chain still moves.
+__device__ __forceinline__ uint32_t long_entry(const uint16_t *lut, uint32_t last, uint32_t t,
                                                uint32_t w32, bool need) {
-    const uint32_t le = walk_tables(lut, last, e & 0x7FFFu, w32, need);
-    const uint32_t len = (le >> 8) ? (le >> 8) : 63u;  // 63: unreachable once phase 1 passed
-    return (1u << 30) | (len << 24) | (le & 0xFFu);
+    const uint32_t le = walk_tables(lut, last, t, w32, need) & 0x3FFFu;
+    const uint32_t e = __builtin_amdgcn_perm(0u, le, 0x010C0C00u) | (1u << 30);
+    return max(e, (1u << 30) | (1u << 24));
 }
 
 // Thread t's C windows: 8*C bytes plus the 4 bytes after them (big-endian
@@ -229,10 +234,14 @@ __device__ __forceinline__ void count_codes(const Windows<C> &W, const uint32_t 
             uint32_t e = *reinterpret_cast<const uint16_t *>(
                 fast + kCountOff + ((w32 >> (32 - DF11_COUNT_BITS)) << 1));
             if (__builtin_expect(e < (1u << 12), 0)) {  // rare: a first code longer than the index
-                const uint32_t len = walk_tables(lut, last, e, w32, true) >> 8;
-                // one code of that length; none at all means a corrupt input
-                bad[c] |= len ? 0u : kBadCount;
-                e = len ? (len << 12) | 1u : (64u << 12);
+                const uint32_t le = walk_tables(lut, last, e, w32, true);
+                // one code of that length (as an entry: length << 12, one start
+                // at offset 0).  A pointer has a zero length field (table
+                // indices are below 64); no leaf, or a zero length, means
+                // damaged tables: the window is flagged and its chain ends.
+                const uint32_t len12 = (le << 4) & 0x3F000u;
+                bad[c] |= len12 ? 0u : kBadCount;
+                e = len12 ? len12 | 1u : (64u << 12);
             }
             cnt[c] += uint32_t(__builtin_popcount(e & 0xFFFu));
             q[c] -= e >> 12;
@@ -542,24 +551,31 @@ struct OutFmt<DF11_FORMAT_BF16> {
 template <int M>
 struct OutFp8 {
     static constexpr uint32_t kChunk = 16;
+    static constexpr uint32_t kSign = 0x80808080u;
+    static constexpr uint32_t kKeep = kSign | (0x01010101u * ((1u << M) - 1u));  // sign and mantissa
     static __device__ __forceinline__ uint32_t rest_off(uint32_t g) { return g >> 1; }
     // four outputs from four nibbles (one per byte of D) and four exponents E
     static __device__ __forceinline__ uint32_t assemble(uint32_t D, uint32_t E) {
         constexpr uint32_t mant = 0x01010101u * ((1u << M) - 1u);
-        return (D & mant) | ((D << (7 - M)) & 0x80808080u) | (E << M);
+        return (D & mant) | ((D << (7 - M)) & kSign) | (E << M);
     }
-    // the 4 nibbles of 2 sm bytes, spread one per byte (sel picks the 2 bytes twice)
-    static __device__ __forceinline__ uint32_t spread(uint32_t S, uint32_t sel) {
-        const uint32_t u = __builtin_amdgcn_perm(S, S, sel);
-        return (u & 0x000F000Fu) | ((u >> 4) & 0x0F000F00u);
+    // Eight outputs from the 8 nibbles of S and 8 exponents (E0: outputs
+    // 0..3, E1: 4..7).  lo holds the even nibbles one per byte and hi the odd
+    // ones, each with its sign bit copied to bit 7 (the other bits above the
+    // mantissa are cleared by kKeep); byte permutes interleave them into
+    // output order.
+    static __device__ __forceinline__ void assemble8(uint32_t S, uint32_t E0, uint32_t E1,
+                                                     uint32_t &o0, uint32_t &o1) {
+        const uint32_t lo = ((S << (7 - M)) & kSign) | (S & ~kSign);
+        const uint32_t hi = ((S << (3 - M)) & kSign) | ((S >> 4) & ~kSign);
+        o0 = (__builtin_amdgcn_perm(hi, lo, 0x05010400u) & kKeep) | (E0 << M);
+        o1 = (__builtin_amdgcn_perm(hi, lo, 0x07030602u) & kKeep) | (E1 << M);
     }
     static __device__ __forceinline__ uint4 chunk(uint2 s8, const uint8_t *ex) {
         const uint4 e16 = *reinterpret_cast<const uint4 *>(ex);
         uint4 v;
-        v.x = assemble(spread(s8.x, 0x01010000u), e16.x);
-        v.y = assemble(spread(s8.x, 0x03030202u), e16.y);
-        v.z = assemble(spread(s8.y, 0x01010000u), e16.z);
-        v.w = assemble(spread(s8.y, 0x03030202u), e16.w);
+        assemble8(s8.x, e16.x, e16.y, v.x, v.y);
+        assemble8(s8.y, e16.z, e16.w, v.z, v.w);
         return v;
     }
     static __device__ __forceinline__ void store_at(const KArgs &a, int64_t base, uint32_t c,
