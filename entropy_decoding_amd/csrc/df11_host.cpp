@@ -6,6 +6,7 @@
 #include "df11.h"
 
 #include <algorithm>
+#include <functional>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -192,51 +193,71 @@ int huffman(const uint64_t counts[kSyms], uint8_t len[kSyms]) {
     return mx;
 }
 
-// Length-limited optimal lengths by package-merge.  Uses the prefix property:
-// the items chosen from every denomination list form a prefix of it, so only
-// the number of packages inside each chosen prefix is needed.
+// Length-limited optimal lengths by boundary package-merge (Katajainen,
+// Moffat and Turpin, "A fast and space-economical algorithm for length-limited
+// coding", 1995): package-merge evaluated lazily.  Level 0 is the deepest
+// denomination (leaves only); the item lists of level j are never stored,
+// only their two newest items ("lookahead chains").  A chain records its
+// weight, the number of leaves among the items of its level up to it, and the
+// chain of the level below that closes the last package up to it.  Advancing
+// the top level 2n - 2 items advances each level below only as far as the
+// packages above need; the chains reached from the top level's last item are
+// then the ends of the chosen prefixes of every level, and leaf i (in
+// ascending weight order) gets one bit per level whose prefix holds more than
+// i leaves.  Ties between a leaf and a package take the leaf.
 int package_merge(const uint64_t counts[kSyms], int limit, uint8_t len[kSyms]) {
     std::vector<int> sym;
     for (int s = 0; s < kSyms; s++)
         if (counts[s]) sym.push_back(s);
-    const size_t n = sym.size();
+    const uint32_t n = uint32_t(sym.size());
     std::stable_sort(sym.begin(), sym.end(),
                      [&](int a, int b) { return counts[a] < counts[b]; });
     std::memset(len, 0, kSyms);
-    // lists[l]: weights and package flags for denomination 2^-l, l = 1..limit
-    std::vector<std::vector<uint64_t>> wt(limit + 1);
-    std::vector<std::vector<uint8_t>> pkg(limit + 1);
-    for (size_t i = 0; i < n; i++) {
-        wt[limit].push_back(counts[sym[i]]);
-        pkg[limit].push_back(0);
+    if (n < 2) return huffman(counts, len);
+    struct Chain {
+        uint64_t weight;
+        uint32_t leaves;  // leaves among the level's items up to this one
+        int below;        // chain of the level below closing the last package (-1: none)
+    };
+    std::vector<Chain> pool;
+    pool.reserve(size_t(limit) * (2 * n + 2));
+    auto make = [&](uint64_t w, uint32_t c, int t) {
+        pool.push_back({w, c, t});
+        return int(pool.size() - 1);
+    };
+    const auto leaf_w = [&](uint32_t i) { return counts[sym[i]]; };
+    // the two newest chains of every level; all levels start with the two
+    // lightest leaves
+    std::vector<int> older(limit), newer(limit);
+    for (int j = 0; j < limit; j++) {
+        older[j] = make(leaf_w(0), 1, -1);
+        newer[j] = make(leaf_w(1), 2, -1);
     }
-    for (int l = limit - 1; l >= 1; l--) {
-        const auto &below = wt[l + 1];
-        size_t np = below.size() / 2, li = 0, pi = 0;
-        while (li < n || pi < np) {
-            uint64_t pw = pi < np ? below[2 * pi] + below[2 * pi + 1] : 0;
-            if (li < n && (pi >= np || counts[sym[li]] <= pw)) {
-                wt[l].push_back(counts[sym[li++]]);
-                pkg[l].push_back(0);
-            } else {
-                wt[l].push_back(pw);
-                pkg[l].push_back(1);
-                pi++;
-            }
+    // next item of level j: the next leaf, or the package of the two newest
+    // items of level j - 1, whichever is lighter (then level j - 1 moves on
+    // by two items)
+    std::function<void(int)> advance = [&](int j) {
+        const Chain cur = pool[newer[j]];
+        if (j == 0) {
+            if (cur.leaves >= n) return;
+            older[0] = newer[0];
+            newer[0] = make(leaf_w(cur.leaves), cur.leaves + 1, -1);
+            return;
         }
-    }
-    size_t take = 2 * n - 2;
+        const uint64_t pkg = pool[older[j - 1]].weight + pool[newer[j - 1]].weight;
+        older[j] = newer[j];
+        if (cur.leaves < n && leaf_w(cur.leaves) <= pkg) {
+            newer[j] = make(leaf_w(cur.leaves), cur.leaves + 1, cur.below);
+        } else {
+            newer[j] = make(pkg, cur.leaves, newer[j - 1]);
+            advance(j - 1);
+            advance(j - 1);
+        }
+    };
+    for (uint32_t k = 2; k < 2 * n - 2; k++) advance(limit - 1);
     int mx = 0;
-    for (int l = 1; l <= limit && take; l++) {
-        size_t packages = 0;
-        for (size_t i = 0; i < take; i++) packages += pkg[l][i];
-        size_t leaves = take - packages;  // the cheapest `leaves` symbols get one more bit
-        for (size_t i = 0; i < leaves; i++) {
-            len[sym[i]]++;
-            mx = std::max<int>(mx, len[sym[i]]);
-        }
-        take = 2 * packages;
-    }
+    for (int c = newer[limit - 1]; c >= 0; c = pool[c].below)
+        for (uint32_t i = 0; i < pool[c].leaves; i++) mx = std::max<int>(mx, ++len[sym[i]]);
     return mx;
 }
 
