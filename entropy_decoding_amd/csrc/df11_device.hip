@@ -666,6 +666,14 @@ __device__ __forceinline__ void wave_tiles(const KArgs &a, Epi &epi, uint32_t fi
     if constexpr (Epi::kAlways) __builtin_amdgcn_s_waitcnt(0x0F70);
     const uint16_t *lut = reinterpret_cast<const uint16_t *>(dyn);
     uint8_t *ebuf = dyn + a.ebuf_off + wid * a.exp_cap;
+    // The FP8 assembly shifts whole dwords of staged exponents, so a staged
+    // byte with bits above the symbol's width would carry into the next
+    // output's mantissa.  Every byte this kernel stages is a symbol, but the
+    // first chunk's bytes below a tile's first output are never written by
+    // that tile and start as whatever LDS held before (another kernel's
+    // data); they are cleared once.
+    if constexpr (FMT != DF11_FORMAT_BF16)
+        if (lane < 4) reinterpret_cast<uint32_t *>(ebuf)[lane] = 0;
 
     for (uint32_t it = slot; it < count; it += n_slots) {
         const uint32_t tile = first + it;
