@@ -255,6 +255,8 @@ def main():
                          "against decompression followed by a library GEMM")
     ap.add_argument("--tokens", type=int, default=64, choices=(16, 32, 48, 64),
                     help="tokens for --fused-gemm")
+    ap.add_argument("--batch", type=int, default=512,
+                    help="vectors of the --pipeline GEMM consumer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decoder needs no cross-GPU exchange (each GPU "
@@ -627,7 +629,7 @@ def pipeline_bench(args, torch, ed, sw):
     on a second stream into the other of two buffers (df11_pipeline_*).
 
     Two consumers: this library's BF16 GEMV (one fp32 vector, memory-bound like
-    decoding one token) and a plain library BF16 GEMM over 512 vectors
+    decoding one token) and a plain library BF16 GEMM over --batch vectors
     (torch.mm, compute-bound like a prefill chunk).  Times per block:
     decompression alone, the consumer alone on resident BF16 weights, both in
     sequence on one stream, and both overlapped."""
@@ -664,8 +666,8 @@ def pipeline_bench(args, torch, ed, sw):
     def gemv(buf, i, out):
         ed.df11_gemv_bf16(buf, layout, x, out[i], torch.cuda.current_stream())
 
-    # consumer 2: GEMM over a batch of 512 BF16 vectors (library GEMM)
-    batch = 512
+    # consumer 2: GEMM over a batch of BF16 vectors (library GEMM; 512 by default)
+    batch = args.batch
     xb = [torch.from_numpy(rng.standard_normal((c, batch)).astype(np.float32)).to(dev)
           .to(torch.bfloat16).contiguous() for _, c in shapes]
     ob = [torch.empty((r, batch), dtype=torch.bfloat16, device=dev) for r, _ in shapes]
