@@ -766,7 +766,7 @@ def pipeline_bench(args, torch, ed, sw):
     achieved = (dec_bytes + gemv_bytes) / (g["pipelined_ms"] * 1e-3) / 1e9
     gm = results[f"gemm_b{batch}"]
     line = {
-        "metric": "pipelined block time (decompress the next block while a GEMM over 512 "
+        "metric": f"pipelined block time (decompress the next block while a GEMM over {batch} "
                   "vectors reads this one)",
         "value": gm["pipelined_ms"], "unit": "ms per block", "n_gpus": 1,
         "steps": passes, "warmup": max(1, min(args.warmup, 3)), "higher_is_better": False,
