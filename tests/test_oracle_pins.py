@@ -105,6 +105,18 @@ def test_huffman_ties_have_equal_cost():
     assert _cost(counts, lens) == 12 == _brute_min_cost([1, 1, 2, 2], 3)
 
 
+def test_golden_tie_rules():
+    # the pages leave ties among equal weights open; the stated rules are
+    # worked by hand in the golden file, so a reversed or reordered tie rule
+    # in the oracle fails here even though its code costs the same
+    for case, limit, *cols in _read_golden("tie_rules.txt"):
+        triples = [tuple(int(v) for v in c.split(":")) for c in cols]
+        counts = _counts({s: w for s, w, _ in triples})
+        lens = oracle.huffman_lengths(counts) if int(limit) == 0 else \
+            oracle.limited_lengths(counts, int(limit))
+        assert [int(lens[s]) for s, _, _ in triples] == [l for _, _, l in triples], case
+
+
 @pytest.mark.parametrize("seed", range(20))
 def test_package_merge_equals_bounded_brute_force(seed):
     rng = np.random.default_rng(100 + seed)
@@ -134,16 +146,23 @@ def _fibonacci_counts(n):
     return _counts(dict(enumerate(f)))
 
 
-def test_length_limit_forced_by_fibonacci_histogram():
-    counts = _fibonacci_counts(40)
+@pytest.mark.parametrize("n", [34, 40])
+def test_length_limit_forced_by_fibonacci_histogram(n):
+    # n Fibonacci weights give the most skewed tree, of depth n - 1: with 34
+    # the unlimited code is exactly one bit over the 32-bit limit
+    counts = _fibonacci_counts(n)
     h = oracle.huffman_lengths(counts)
-    assert h.max() == 39  # natural depth n - 1
+    assert h.max() == n - 1
     lens = oracle.code_lengths(counts)
     assert lens.max() == 32
     assert oracle.kraft_numerator(lens) == 1 << 32
     assert _cost(counts, lens) >= _cost(counts, h)
     # still optimal among codes with l <= 32: package-merge at 32 vs at 33..39 is monotone
     assert _cost(counts, oracle.limited_lengths(counts, 33)) <= _cost(counts, lens)
+    if n == 34:
+        # the same histogram as BF16 weights: the codebook applies the limit too
+        w = np.repeat(np.arange(n, dtype=np.uint16) << 7, [int(c) for c in counts[:n]])
+        assert oracle.codebook(w).lens.max() == 32
 
 
 # ------------------------------------------------------------ invariants
@@ -273,10 +292,14 @@ def test_round_trip_small_sizes(n):
 
 def test_sign_mantissa_byte_layout_from_the_bf16_fields():
     # sign is bit 15, exponent bits 14..7, mantissa bits 6..0 of a BF16 pattern
-    w = np.array([0b1_10000001_0101010, 0b0_01111111_1111111], dtype=np.uint16)
+    # (the last two have a sign unlike the exponent's top bit)
+    w = np.array([0b1_10000001_0101010, 0b0_01111111_1111111,
+                  0b1_01111111_0000001, 0b0_10000000_1000000], dtype=np.uint16)
     cb, enc = _round_trip(w)
-    assert enc.sm.tolist() == [0b1_0101010, 0b0_1111111]
-    assert oracle.exponents(w).tolist() == [0b10000001, 0b01111111]
+    sm = [0b1_0101010, 0b0_1111111, 0b1_0000001, 0b0_1000000]
+    assert enc.sm.tolist() == sm
+    assert oracle.sign_mantissa(w).tolist() == sm
+    assert oracle.exponents(w).tolist() == [0b10000001, 0b01111111, 0b01111111, 0b10000000]
 
 
 # ------------------------------------------------------------ aux arrays
@@ -507,6 +530,14 @@ def test_fp8_uniform_exponents_give_fixed_width_codes(fmt, width):
     bits = "".join(format(int(s), f"0{width}b") for s in e)
     assert total == len(bits) and len(bits) % 8 == 0
     assert stream.tobytes() == int(bits, 2).to_bytes(len(bits) // 8, "big")
+    # tiles of total / 64 windows of 8 bytes hold the stream exactly: one tile
+    # with every code, and window j's first code at the first multiple of the
+    # width at or after bit 64 j
+    T = total // 64
+    assert T * 64 == total
+    gaps, bop = oracle.aux_symbols(sym, cb, T, 8)
+    assert bop.tolist() == [0, e.size]
+    assert gaps.tolist() == [(-64 * j) % width for j in range(T)]
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
