@@ -9,7 +9,7 @@ written, whole job over K steps), plus the dominant kernel's HBM roofline
 fraction from algorithmic bytes (compressed arrays read once + BF16 written)
 and the CPU oracle's bit-serial decode timed on this host as a baseline.
 
-  python bench.py [--steps K] [--warmup W] [--config 2|1|0|3a|3b|3c|4] [--tile-windows 64|256|512]
+  python bench.py [--steps K] [--warmup W] [--config 2|1|0|2tp8|3a|3b|3c|4] [--tile-windows 64|256|512]
   python bench.py --pipeline     # 8B model blocks, next block decompressed while a GEMV reads this one
   python bench.py --fused        # y = W x straight from the compressed block vs decompress + GEMV
   python bench.py --fused-gemm   # Y = X W^T for 16-64 tokens on the matrix cores, same comparison
@@ -235,7 +235,7 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="keep the GPU busy this long before the warm-up steps (clock ramp)")
     ap.add_argument("--no-extra-configs", dest="extra_configs", action="store_false",
-                    help="skip timing configs 0, 1, 3a-c after the 70B block")
+                    help="skip timing configs 0, 1, 2tp8, 3a-c after the 70B block")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes instead "
                          "(the achievable-bandwidth reference and the counter calibration)")
@@ -373,7 +373,7 @@ def other_configs(args, torch, ed, sw) -> dict:
     steps with the caches evicted between steps) and compared with the
     original bits."""
     res = {}
-    for k in ("0", "1", "3a", "3b", "3c"):
+    for k in ("0", "1", "2tp8", "3a", "3b", "3c"):
         cfg = sw.config(k)
         unit = cfg.units[0]
         tensors, name = gen_workload(unit, cfg, args, sw)

@@ -55,6 +55,21 @@ LLAMA3_70B_BLOCK = [
     ("down_proj", (8192, 28672)),
 ]
 
+# One GPU's share of the 70B-shaped block under 8-way tensor parallelism in
+# the usual layout: the projections that feed a nonlinearity or attention (q,
+# k, v, gate, up) split their output rows, the two that feed the residual
+# stream (o, down) split their input columns.  Each shard row is drawn with the
+# full block's per-row recipe, which is what slicing the full matrix would give.
+LLAMA3_70B_BLOCK_TP8 = [
+    ("q_proj", (1024, 8192)),
+    ("k_proj", (128, 8192)),
+    ("v_proj", (128, 8192)),
+    ("o_proj", (8192, 1024)),
+    ("gate_proj", (3584, 8192)),
+    ("up_proj", (3584, 8192)),
+    ("down_proj", (8192, 3584)),
+]
+
 VOCAB_SHAPE = (128256, 4096)
 STRESS_SHAPE = (4096, 14336)
 
@@ -87,7 +102,8 @@ class Config:
 
 def config(k: int | str) -> Config:
     """The five workloads: 0 small tensor, 1 8B block, 2 70B block,
-    3 distribution stress (3a/3b/3c as units), 4 full 8B model."""
+    3 distribution stress (3a/3b/3c as units), 4 full 8B model; and 2tp8,
+    one GPU's share of the 70B block under 8-way tensor parallelism."""
     k = str(k)
     if k == "0":
         return Config(0, "tensor_1024x1024_gauss",
@@ -98,6 +114,9 @@ def config(k: int | str) -> Config:
     if k == "2":
         return Config(2, "llama3_70b_block",
                       [Unit("block", LLAMA3_70B_BLOCK, "lognormal_rows", 2)])
+    if k == "2tp8":
+        return Config(2, "llama3_70b_block_tp8_shard",
+                      [Unit("block_tp8_rank0", LLAMA3_70B_BLOCK_TP8, "lognormal_rows", 22)])
     if k in ("3", "3a", "3b", "3c"):
         units = [
             Unit("3a_student_t_outliers", [("w", STRESS_SHAPE)], "student_t_outliers", 30),
