@@ -9,7 +9,7 @@ written, whole job over K steps), plus the dominant kernel's HBM roofline
 fraction from algorithmic bytes (compressed arrays read once + BF16 written)
 and the CPU oracle's bit-serial decode timed on this host as a baseline.
 
-  python bench.py [--steps K] [--warmup W] [--config 2|1|0|2tp8|3a|3b|3c|4] [--tile-windows 64|256|512]
+  python bench.py [--steps K] [--warmup W] [--config 2|1|0|2tp8|405tp8|3a|3b|3c|4] [--tile-windows 64|256|512]
   python bench.py --pipeline     # 8B model blocks, next block decompressed while a GEMV reads this one
   python bench.py --fused        # y = W x straight from the compressed block vs decompress + GEMV
   python bench.py --fused-gemm   # Y = X W^T for 16-64 tokens on the matrix cores, same comparison
@@ -235,7 +235,7 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="keep the GPU busy this long before the warm-up steps (clock ramp)")
     ap.add_argument("--no-extra-configs", dest="extra_configs", action="store_false",
-                    help="skip timing configs 0, 1, 2tp8, 3a-c after the 70B block")
+                    help="skip timing configs 0, 1, 2tp8, 405tp8, 3a-c after the 70B block")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="time a plain device-to-device copy of this many bytes instead "
                          "(the achievable-bandwidth reference and the counter calibration)")
@@ -363,7 +363,7 @@ def gen_workload(unit, cfg, args, sw):
 
 def gpu_marketing_name() -> str:
     """The first GPU agent's marketing name from rocminfo ('' if unavailable):
-    the device properties' name is empty on some ROCm builds."""
+    the device properties' name is empty or generic on some ROCm builds."""
     try:
         out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
     except (OSError, subprocess.SubprocessError):
@@ -380,7 +380,7 @@ def gpu_marketing_name() -> str:
 
 def system_info(torch) -> dict:
     p = torch.cuda.get_device_properties(0)
-    return {"gpu": p.name or gpu_marketing_name(), "arch": getattr(p, "gcnArchName", ""),
+    return {"gpu": gpu_marketing_name() or p.name, "arch": getattr(p, "gcnArchName", ""),
             "cus": p.multi_processor_count, "torch": torch.__version__,
             "hip": getattr(torch.version, "hip", None)}
 
@@ -391,7 +391,7 @@ def other_configs(args, torch, ed, sw) -> dict:
     steps with the caches evicted between steps) and compared with the
     original bits."""
     res = {}
-    for k in ("0", "1", "2tp8", "3a", "3b", "3c"):
+    for k in ("0", "1", "2tp8", "405tp8", "3a", "3b", "3c"):
         cfg = sw.config(k)
         unit = cfg.units[0]
         tensors, name = gen_workload(unit, cfg, args, sw)

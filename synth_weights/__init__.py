@@ -70,6 +70,18 @@ LLAMA3_70B_BLOCK_TP8 = [
     ("down_proj", (8192, 3584)),
 ]
 
+# The same share of a Llama-3.1-405B-shaped block (hidden 16384, intermediate
+# 53248, 8 key/value heads of 128), the largest model the pages name.
+LLAMA31_405B_BLOCK_TP8 = [
+    ("q_proj", (2048, 16384)),
+    ("k_proj", (128, 16384)),
+    ("v_proj", (128, 16384)),
+    ("o_proj", (16384, 2048)),
+    ("gate_proj", (6656, 16384)),
+    ("up_proj", (6656, 16384)),
+    ("down_proj", (16384, 6656)),
+]
+
 VOCAB_SHAPE = (128256, 4096)
 STRESS_SHAPE = (4096, 14336)
 
@@ -102,8 +114,9 @@ class Config:
 
 def config(k: int | str) -> Config:
     """The five workloads: 0 small tensor, 1 8B block, 2 70B block,
-    3 distribution stress (3a/3b/3c as units), 4 full 8B model; and 2tp8,
-    one GPU's share of the 70B block under 8-way tensor parallelism."""
+    3 distribution stress (3a/3b/3c as units), 4 full 8B model; and 2tp8 and
+    405tp8, one GPU's share of the 70B and of a 405B-shaped block under 8-way
+    tensor parallelism."""
     k = str(k)
     if k == "0":
         return Config(0, "tensor_1024x1024_gauss",
@@ -117,6 +130,9 @@ def config(k: int | str) -> Config:
     if k == "2tp8":
         return Config(2, "llama3_70b_block_tp8_shard",
                       [Unit("block_tp8_rank0", LLAMA3_70B_BLOCK_TP8, "lognormal_rows", 22)])
+    if k == "405tp8":
+        return Config(2, "llama31_405b_block_tp8_shard",
+                      [Unit("block_tp8_rank0", LLAMA31_405B_BLOCK_TP8, "lognormal_rows", 23)])
     if k in ("3", "3a", "3b", "3c"):
         units = [
             Unit("3a_student_t_outliers", [("w", STRESS_SHAPE)], "student_t_outliers", 30),

@@ -383,7 +383,7 @@ def test_stress_config_full_size(cfg, unit_tensors):
     check_sampled_tiles(u, out)
 
 
-@pytest.mark.parametrize("cfg,tw", [("1", 64), ("1", 256), ("2", 64), ("2tp8", 64)])
+@pytest.mark.parametrize("cfg,tw", [("1", 64), ("1", 256), ("2", 64), ("2tp8", 64), ("405tp8", 64)])
 def test_block_config_full_size(cfg, tw):
     unit = sw.config(cfg).units[0]
     tensors = sw.gen_unit(unit)
