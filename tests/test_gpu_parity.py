@@ -373,6 +373,30 @@ def test_launch_on_a_side_stream(unit_tensors):
     assert torch.equal(out, _dev_i16(w))
 
 
+def test_concurrent_launches_on_two_streams(unit_tensors):
+    # the library holds no state between calls: two units decoded on two
+    # streams at once, launches interleaved, each equal to its original
+    (w0,) = unit_tensors("0")
+    rng = np.random.default_rng(21)
+    w1 = ((rng.standard_normal(700_001).astype(np.float32) * 0.05).view(np.uint32) >> 16).astype(np.uint16)
+    units = [Unit([w0]), Unit([w1])]
+    refs = [_dev_i16(w0), _dev_i16(w1)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.zeros(u.n, dtype=torch.int16, device="cuda") for _ in range(4)] for u in units]
+    status = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in units]
+    torch.cuda.synchronize()
+    say("[gpu] two units decoded concurrently on two streams")
+    for i in range(4):
+        for k in (0, 1):
+            with torch.cuda.stream(streams[k]):
+                ed.df11_decompress_block(units[k].ds, outs[k][i], status[k], stream=streams[k])
+    torch.cuda.synchronize()
+    for k in (0, 1):
+        assert int(status[k].item()) == 0
+        for i in range(4):
+            assert torch.equal(outs[k][i], refs[k]), f"unit {k} launch {i}"
+
+
 # ------------------------------------------------------------------ full workloads
 
 
