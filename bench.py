@@ -361,28 +361,10 @@ def gen_workload(unit, cfg, args, sw):
     return tensors, workload
 
 
-def gpu_marketing_name() -> str:
-    """The first GPU agent's marketing name from rocminfo ('' if unavailable):
-    the device properties' name is empty or generic on some ROCm builds."""
-    try:
-        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
-    except (OSError, subprocess.SubprocessError):
-        return ""
-    name = ""
-    for line in out.splitlines():
-        line = line.strip()
-        if line.startswith("Marketing Name:"):
-            name = line.split(":", 1)[1].strip()
-        elif line.startswith("Device Type:") and line.split(":", 1)[1].strip() == "GPU":
-            return name
-    return ""
-
-
 def system_info(torch) -> dict:
     p = torch.cuda.get_device_properties(0)
-    return {"gpu": gpu_marketing_name() or p.name, "arch": getattr(p, "gcnArchName", ""),
-            "cus": p.multi_processor_count, "torch": torch.__version__,
-            "hip": getattr(torch.version, "hip", None)}
+    return {"gpu": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
 
 
 def other_configs(args, torch, ed, sw) -> dict:
