@@ -176,6 +176,22 @@ def test_fp8_long_tiles_take_the_general_store_path(fmt):
     check_identity(v, "ordinary tiles")
 
 
+def test_fp8_e5m2_long_codes_walk_four_table_levels():
+    # Fibonacci counts over the 32 E5M2 exponent values give the most skewed
+    # code, 31 bits long at the deepest, resolved through four table levels
+    f = [1, 1]
+    while len(f) < 32:
+        f.append(f[-1] + f[-2])
+    rng = np.random.default_rng(31)
+    e = np.repeat(np.arange(32, dtype=np.uint8), f)
+    rng.shuffle(e)
+    b = ((e << 2) | rng.integers(0, 4, e.size, dtype=np.uint8)
+         | (rng.integers(0, 2, e.size, dtype=np.uint8) << 7)).astype(np.uint8)
+    u = Unit([b], "fp8_e5m2")
+    assert u.cb.max_len == 31 and u.cb.n_luts == 4
+    check_identity(u, "31-bit codes")
+
+
 def test_fp8_requires_64_window_tiles_and_8_bit_outputs(unit_tensors):
     (w,) = unit_tensors("0")
     u = Unit([_fp8(w, "fp8_e5m2")], "fp8_e5m2")
